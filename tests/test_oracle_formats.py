@@ -1,0 +1,148 @@
+"""Pins for the oracle's packed layouts (CPU only).
+
+The layouts are this library's own; the pins are hand-worked bytes from the
+layout text, round trips, word invariants, and the add-only identity that ties
+the weight layout to the activation bit planes."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _words(packed):
+    return np.asarray(packed, dtype=np.uint8).view("<u4")
+
+
+# ----------------------------------------------------------------------------- T2-PN-64
+@pytest.mark.parametrize("n,k,code,byte,value", [
+    (0, 0, +1, 0, 0x01),      # P0 of row 0, c = 0 -> bit 0
+    (0, 4, +1, 0, 0x02),      # c = 4 = 4*1 + 0 -> bit 1
+    (0, 1, -1, 9, 0x01),      # N0 starts at byte 8; c = 1 -> bit 8 -> byte 9 bit 0
+    (0, 31, -1, 11, 0x80),    # c = 31 = 4*7 + 3 -> bit 31 of N0 -> byte 11 bit 7
+    (1, 33, +1, 21, 0x01),    # row 1 at byte 16; P1 at +4; c = 1 -> byte 21 bit 0
+    (63, 63, +1, 16 * 63 + 7, 0x80),   # row 63, P1, c = 31 -> bit 31 -> byte 7 of the row
+    (0, 64, +1, 1024, 0x01),  # tile (0, 1)
+    (64, 0, -1, 2048 + 8, 0x01),  # tile (1, 0) with K = 128 -> byte 2 * 1024
+])
+def test_t2_worked_bytes(n, k, code, byte, value):
+    codes = np.zeros((128, 128), dtype=np.int8)
+    codes[n, k] = code
+    packed = oracle.pack_ternary(codes)
+    expect = np.zeros_like(packed)
+    expect[byte] = value
+    assert np.array_equal(packed, expect)
+
+
+def test_t2_round_trip_and_invariants():
+    codes = synth.ternary_codes(synth.matrix_key(0, 99, 0, 0), 192, 320)
+    packed = oracle.pack_ternary(codes)
+    assert packed.size == 192 * 320 // 4 == oracle.ternary_packed_bytes(192, 320)
+    assert np.array_equal(oracle.unpack_ternary(packed, 192, 320), codes)
+    w = _words(packed).reshape(-1, 4)                  # [P0, P1, N0, N1] per tile row
+    assert not np.any(w[:, 0] & w[:, 2]) and not np.any(w[:, 1] & w[:, 3])
+    pop = lambda a: int(sum(bin(int(v)).count("1") for v in a.ravel()))
+    assert pop(w[:, :2]) == int(np.count_nonzero(codes == 1))
+    assert pop(w[:, 2:]) == int(np.count_nonzero(codes == -1))
+
+
+def test_t2_all_plus_row():
+    codes = np.zeros((64, 64), dtype=np.int8)
+    codes[5] = 1
+    w = _words(oracle.pack_ternary(codes)).reshape(64, 4)
+    assert list(w[5]) == [0xFFFFFFFF, 0xFFFFFFFF, 0, 0]
+    assert not np.any(np.delete(w, 5, axis=0))
+
+
+def test_t2_invalid_codes():
+    codes = np.zeros((64, 64), dtype=np.int8)
+    codes[0, :3] = [2, -5, 1]
+    packed, bad = oracle.pack_ternary(codes, count_invalid=True)
+    assert bad == 2
+    back = oracle.unpack_ternary(packed, 64, 64)
+    assert list(back[0, :3]) == [0, 0, 1]
+    # a (P, N) = (1, 1) pair is invalid on unpack and decodes to 0
+    packed = packed.copy()
+    packed[0] |= 0x01
+    packed[8] |= 0x01
+    codes2, bad2 = oracle.unpack_ternary(packed, 64, 64, count_invalid=True)
+    assert bad2 == 1 and codes2[0, 0] == 0
+
+
+# ----------------------------------------------------------------------------- S1-128
+@pytest.mark.parametrize("n,k,byte,value", [
+    (0, 0, 0, 0x01),       # c = 0 -> bit 0
+    (0, 1, 2, 0x01),       # c = 1 = 2*0+1 -> bit 16 -> byte 2 bit 0
+    (0, 2, 0, 0x02),       # c = 2 -> p = 1 -> bit 1
+    (0, 33, 6, 0x01),      # word 1 (bytes 4..7), c = 1 -> bit 16 -> byte 6
+    (1, 31, 19, 0x80),     # row 1 at 16; c = 31 -> bit 31 -> byte 19 bit 7
+    (0, 128, 1024, 0x01),  # tile (0, 1)
+])
+def test_s1_worked_bytes(n, k, byte, value):
+    W = np.ones((64, 256), dtype=np.float32)
+    W[n, k] = -0.25
+    packed = oracle.pack_sign(W)
+    expect = np.zeros_like(packed)
+    expect[byte] = value
+    assert np.array_equal(packed, expect)
+
+
+def test_s1_round_trip_and_zero_reading():
+    W = synth.normal_fp32((128, 384), 0, 98, 1)
+    W[0, :4] = [0.0, -0.0, np.nan, -np.inf]
+    S = oracle.unpack_sign(oracle.pack_sign(W), 128, 384)
+    expect = np.where(W < 0, -1, 1)
+    assert np.array_equal(S, expect)
+    assert list(S[0, :4]) == [1, 1, 1, -1]
+    assert oracle.pack_sign(W).size == 128 * 384 // 8
+
+
+# ----------------------------------------------------------------------------- X8-64 planes
+def test_planes_worked_bits():
+    q = np.zeros((1, 64), dtype=np.int8)
+    q[0, 0] = 1
+    q[0, 5] = -128            # 0x80: plane 7 only; c = 5 = 4*1 + 1 -> bit 9
+    q[0, 40] = 3              # h = 1, c = 8 = 4*2 + 0 -> bit 2; planes 0 and 1
+    X = oracle.act_planes(q)[0, 0]
+    expect = np.zeros(16, dtype=np.uint32)
+    expect[2 * 0 + 0] |= 1 << 0
+    expect[2 * 7 + 0] |= 1 << 9
+    expect[2 * 0 + 1] |= 1 << 2
+    expect[2 * 1 + 1] |= 1 << 2
+    assert np.array_equal(X, expect)
+
+
+def _popcount32(a):
+    a = a.astype(np.uint64)
+    c = np.zeros_like(a)
+    for b in range(32):
+        c += (a >> np.uint64(b)) & np.uint64(1)
+    return c.astype(np.int64)
+
+
+def test_add_only_identity_ties_layouts_together():
+    """sum_b c_b * popcount((P & X_b) | (N & ~X_b)) + popcount(N) == sum_k w_k q_k,
+    with c_b = 2^b (b < 7) and c_7 = -128: the identity the add-only GEMV evaluates.
+    A wrong bit order in either the weight layout or the planes breaks it."""
+    M, N, K = 3, 64, 192
+    rg = synth.rng(0, 97)
+    q = rg.integers(-128, 128, size=(M, K)).astype(np.int8)
+    codes = synth.ternary_codes(synth.matrix_key(0, 97, 0, 1), N, K)
+    w = _words(oracle.pack_ternary(codes)).reshape(N // 64, K // 64, 64, 4)   # [tn, tk, r, word]
+    X = oracle.act_planes(q)                                                  # [m, t, 16]
+    cb = [1, 2, 4, 8, 16, 32, 64, -128]
+    acc = np.zeros((M, N), dtype=np.int64)
+    for m in range(M):
+        for t in range(K // 64):
+            P = w[0, t, :, 0:2]
+            Nn = w[0, t, :, 2:4]
+            for b in range(8):
+                xb = X[m, t, 2 * b: 2 * b + 2][None, :]
+                sel = (P & xb) | (Nn & ~xb)
+                acc[m] += cb[b] * _popcount32(sel).sum(axis=1)
+            acc[m] += _popcount32(Nn).sum(axis=1)
+    brute = np.zeros((M, N), dtype=np.int64)
+    for m in range(M):
+        for n in range(N):
+            brute[m, n] = sum(int(codes[n, k]) * int(q[m, k]) for k in range(K))
+    assert np.array_equal(acc, brute)
