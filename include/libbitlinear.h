@@ -1,0 +1,184 @@
+/*
+ * libbitlinear — ternary (BitNet b1.58) and sign-only (OneBit) linear layers for
+ * AMD Instinct MI355X (gfx950), as a C ABI over hand-written HIP kernels.
+ *
+ * Sources (cited by page title and section):
+ *  [b158]   "微软、国科大开启1Bit时代：大模型转三进制，速度快4倍能耗降至1/41" — BitNet b1.58
+ *           write-up. "BitNet b1.58 介绍": weights in {-1, 0, +1}, BitLinear replaces
+ *           nn.Linear, per-token activations scaled into [-Q_b, Q_b] without a zero point,
+ *           no biases. "实验及结果": the matrix product reduces to int8 additions (Fig. 3)
+ *           and latency was measured with a 2-bit kernel (Fig. 2).
+ *  [onebit] "清华、哈工大把大模型压缩到了1bit，把大模型放在手机里跑的愿望就快要实现了！" —
+ *           OneBit write-up. "OneBit 框架 / 1. 新的1bit结构" (Fig. 3): +-1 weight matrix plus
+ *           two FP16 value vectors g, h; y = ((x ⊙ g) · sign(W)^T) ⊙ h; the 4096x4096 storage
+ *           count. "3. 通过知识蒸馏迁移原模型能力": only Sign(W) is kept for inference.
+ *           "讨论与分析 / 1. 效率": the element products become bit assignments plus additions.
+ *
+ * Conventions for every entry point:
+ *  - Shapes follow nn.Linear: x is [M, K] row-major (M tokens, K inputs), the weight is
+ *    [N, K] (N outputs), y is [M, N] row-major fp32. No bias.
+ *  - Every pointer argument is a DEVICE pointer on the current HIP device unless stated.
+ *    fp16 values are passed as uint16_t IEEE binary16 bit patterns.
+ *  - The caller owns every buffer. The library allocates nothing, frees nothing and keeps
+ *    no pointer after returning. All work is queued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and is asynchronous: a return of BL_OK means the work was queued.
+ *  - Arguments are checked on the host before anything is queued; a failed check returns
+ *    its status and queues nothing. A failed launch returns BL_ERR_HIP and
+ *    bl_last_error() (thread-local) holds the HIP error text. Nothing aborts or throws.
+ *  - Conditions that depend on data values cannot be reported synchronously; they yield
+ *    the defined outputs stated per function.
+ *  - Workspace: ops that split K across workgroups use `ws`, a device buffer of at least
+ *    bl_workspace_bytes(M, N, K) bytes that must be zero-filled before its first use
+ *    (bl_workspace_clear or any fill). Every call leaves the bytes it used zero again.
+ *    Calls that share one workspace must not overlap in time (same stream, or synchronised).
+ *  - Results are deterministic: the integer paths give identical bits on every run and the
+ *    fp32 paths use a fixed summation order for a given shape.
+ *
+ * Packed layouts (the pages fix only 2 bits per ternary weight, 1 bit per sign weight):
+ *  T2-PN-64 (ternary). N % 64 == 0, K % 64 == 0. Tile (tn, tk) = rows 64tn..+63, inputs
+ *    64tk..+63, 1024 bytes at byte (tn*(K/64) + tk)*1024. Row r of a tile = bytes
+ *    16r..16r+15 = little-endian uint32 [P0, P1, N0, N1]. Word X_h covers inputs
+ *    k = 64tk + 32h + c (c = 0..31); c = 4j + i is bit 8i + j. P bit set iff w = +1, N bit
+ *    set iff w = -1, both clear iff w = 0 (both set: invalid). N*K/4 bytes.
+ *  X8-64 (int8 activation bit planes). Row m, 64-input tile t: 16 uint32 words at word
+ *    (m*(K/64) + t)*16; word 2b + h holds bit b (two's complement, b = 0..7) of
+ *    q[m, 64t + 32h + c] at the same bit positions as T2-PN-64. M*K bytes.
+ *  S1-128 (sign). N % 64 == 0, K % 128 == 0. Tile (tn, tk) = rows 64tn..+63, inputs
+ *    128tk..+127, 1024 bytes at byte (tn*(K/128) + tk)*1024. Row r = bytes 16r..16r+15 =
+ *    uint32 W_0..W_3; W_h covers k = 128tk + 32h + c; c = 2p is bit p and c = 2p+1 is
+ *    bit 16+p (p = 0..15). Bit set iff the weight is -1. N*K/8 bytes.
+ */
+#ifndef LIBBITLINEAR_H
+#define LIBBITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+enum bl_status {
+  BL_OK = 0,
+  BL_ERR_NULL = 1,       /* a required pointer is NULL */
+  BL_ERR_SHAPE = 2,      /* a size is < 1, too large, or not the multiple its layout needs */
+  BL_ERR_ALIGN = 3,      /* a pointer lacks the 16-byte alignment its loads need */
+  BL_ERR_ALIAS = 4,      /* an output buffer overlaps an input or another output */
+  BL_ERR_WORKSPACE = 5,  /* ws is NULL or smaller than bl_workspace_bytes() */
+  BL_ERR_HIP = 6,        /* a HIP runtime call or launch failed; see bl_last_error() */
+  BL_ERR_ARG = 7         /* any other invalid argument (e.g. an unknown path, beta_len) */
+};
+
+enum bl_path { BL_PATH_AUTO = 0, BL_PATH_GEMV = 1, BL_PATH_GEMM = 2 };
+
+/* Static English text for a status code (never NULL). */
+const char* bl_status_string(int status);
+/* Thread-local text of the last HIP failure seen by this thread ("" if none). */
+const char* bl_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int bl_version(void);
+
+/* ---- size queries (pure host functions; 0 for invalid shapes) ---------------------------- */
+size_t bl_ternary_packed_bytes(int64_t N, int64_t K);   /* N*K/4, T2-PN-64 */
+size_t bl_sign_packed_bytes(int64_t N, int64_t K);      /* N*K/8, S1-128 */
+size_t bl_act_planes_bytes(int64_t M, int64_t K);       /* M*K, X8-64 */
+/* Bytes of zero-filled workspace that any op below needs for an [M,K] x [N,K]^T product
+ * (and bl_ternarize_absmean for an [N,K] matrix). */
+size_t bl_workspace_bytes(int64_t M, int64_t N, int64_t K);
+/* Queue a zero fill of ws[0:bytes) (a kernel, not a memset, so it may be graph-captured). */
+int bl_workspace_clear(void* ws, size_t bytes, void* stream);
+
+/* ---- offline weight preparation ----------------------------------------------------------- */
+
+/* Absmean ternarisation of a float weight [N, K] ([b158] "BitNet b1.58 介绍": ternary
+ * weights; the page gives no formula, the reading is absmean):
+ *   beta = the fp32 value nearest mean_{n,k} |W[n,k]| (exact sum, single rounding);
+ *   code = clip(rne(fl32(W / beta)), -1, 1), decided in fp32.
+ * W fp32 [N, K] row-major (16-byte aligned). Outputs (each may be NULL, not both):
+ * codes int8 [N, K]; packed T2-PN-64 [N*K/4]. beta: one fp32 (device) written always.
+ * Requires N % 64 == 0, K % 64 == 0, N*K < 2^32. If W holds NaN/inf, beta = NaN and every
+ * code is 0; if beta == 0 every code is 0. Uses ws (bl_workspace_bytes(1, N, K)). */
+int bl_ternarize_absmean(const float* W, int64_t N, int64_t K, int8_t* codes, void* packed,
+                         float* beta, void* ws, size_t ws_bytes, void* stream);
+
+/* Pack int8 ternary codes [N, K] into T2-PN-64 ([b158] ternary weights at 2 bits each,
+ * "实验及结果"). A code other than -1/0/+1 packs as 0 and adds 1 to *n_invalid (device
+ * int32, may be NULL). N % 64 == 0, K % 64 == 0; codes and packed 16-byte aligned. */
+int bl_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* packed,
+                    int32_t* n_invalid, void* stream);
+/* Inverse of bl_pack_ternary. A (P, N) = (1, 1) pair decodes to 0 and adds 1 to
+ * *n_invalid (may be NULL). */
+int bl_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes,
+                      int32_t* n_invalid, void* stream);
+
+/* Pack the signs of a float weight [N, K] into S1-128 ([onebit] "3. 通过知识蒸馏迁移原模型
+ * 能力": Sign(W) is what inference keeps). Bit set iff W < 0, so +0, -0 and NaN give +1.
+ * N % 64 == 0, K % 128 == 0; W and packed 16-byte aligned. */
+int bl_pack_sign(const float* W, int64_t N, int64_t K, void* packed, void* stream);
+/* Inverse of bl_pack_sign: int8 signs [N, K] in {-1, +1}. */
+int bl_unpack_sign(const void* packed, int64_t N, int64_t K, int8_t* signs, void* stream);
+
+/* ---- b1.58 forward ------------------------------------------------------------------------- */
+
+/* Per-token absmax int8 quantiser ([b158] "BitNet b1.58 介绍": per-token range
+ * [-Q_b, Q_b], no zero point; Q_b = 127):
+ *   gamma[m] = max_k |x[m,k]|;  q[m,k] = clip(rne(fl32(fl32(127*x) / gamma[m])), -127, 127);
+ *   rowsum[m] = sum_k q[m,k];  planes = X8-64 bit planes of q.
+ * x fp16 [M, K] (16-byte aligned). Outputs: gamma fp32 [M] (required); q int8 [M, K],
+ * rowsum int32 [M], planes uint32 [M*K/4] (each may be NULL; q or planes must be given).
+ * K % 64 == 0. A row holding NaN/inf gets gamma = NaN and q = 0; an all-zero row gets
+ * gamma = 0 and q = 0. */
+int bl_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* gamma,
+                      int32_t* rowsum, uint32_t* planes, void* stream);
+
+/* Add-only decode GEMV ([b158] "实验及结果", Fig. 3: int8 additions only; [onebit]
+ * "讨论与分析 / 1. 效率": bit operations plus additions). For M <= 4:
+ *   acc[m,n] = sum_k w[n,k] q[m,k] (int32, by popcount additions over the X8-64 planes);
+ *   y[m,n] = acc[m,n] * (gamma[m] / 127) * beta[beta_len == 1 ? 0 : n].
+ * planes from bl_quant_act_int8, gamma [M], wpacked T2-PN-64 [N, K], beta fp32 [beta_len]
+ * with beta_len 1 (per tensor) or N (e.g. stacked q/k/v), y fp32 [M, N]. 1 <= M <= 4,
+ * N % 64 == 0, K % 64 == 0. Uses ws. */
+int bl_bitlinear_gemv(const uint32_t* planes, const float* gamma, int64_t M, int64_t K,
+                      const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                      float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Batched / prefill GEMM with int8 matrix cores ([b158] "实验及结果": batched throughput at
+ * sequence length 512). Same result as bl_bitlinear_gemv for any M >= 1: the packed
+ * weights are expanded to int8 tiles in LDS and multiplied by q with int32 accumulation.
+ * q int8 [M, K] (16-byte aligned rows), other arguments as bl_bitlinear_gemv. Uses ws. */
+int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                      const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                      float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Debug: the int32 accumulators acc[m,n] = sum_k w[n,k] q[m,k] of the chosen kernel path,
+ * before the epilogue. path BL_PATH_GEMV needs planes (M <= 4), BL_PATH_GEMM needs q,
+ * BL_PATH_AUTO takes the path bl_bitlinear_forward would take (and needs its operand).
+ * acc int32 [M, N]. Uses ws. */
+int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int64_t K,
+                         const void* wpacked, int64_t N, int32_t* acc, int path, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* The whole b1.58 linear from fp16 activations: quantise, then GEMV (M <= 2) or GEMM, then
+ * rescale. x fp16 [M, K]; other arguments as bl_bitlinear_gemm. path selects the kernel
+ * (BL_PATH_AUTO picks by M). Uses ws (bl_workspace_bytes(M, N, K)), which also holds the
+ * quantised activations. */
+int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
+                         const float* beta, int64_t beta_len, int64_t N, float* y, int path,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---- OneBit forward ------------------------------------------------------------------------ */
+
+/* OneBit linear ([onebit] "1. 新的1bit结构", Fig. 3): y = ((x ⊙ g) · S^T) ⊙ h with
+ * S = sign(W) in S1-128, g fp16 [K] (one per input), h fp16 [N] (one per output),
+ * x fp16 [M, K] unquantised, y fp32 [M, N]. t = x*g is exact in fp32; each +-t is t with
+ * its sign bit set from the packed bit ("bit assignment"), summed in fp32 in a fixed order.
+ * N % 64 == 0, K % 128 == 0. Uses ws. */
+int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked,
+                     const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y, void* ws,
+                     size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBBITLINEAR_H */

@@ -1,0 +1,317 @@
+"""Python binding of libbitlinear: BitNet b1.58 ternary and OneBit sign-only linear layers
+on MI355X (gfx950).
+
+Every function here only marshals arguments: it checks tensor dtypes, devices and
+contiguity, allocates outputs with torch (device memory is PyTorch's job) and calls the
+C entry point of the same name on the current HIP stream. All arithmetic happens in the
+library's HIP kernels. Importing this module fails loudly if the library is not built.
+
+See include/libbitlinear.h for the contract of each call (shapes, layouts, errors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbitlinear.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "libbitlinear.h")
+
+BL_PATH_AUTO, BL_PATH_GEMV, BL_PATH_GEMM = 0, 1, 2
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, where: str, lib):
+        msg = lib.bl_status_string(status).decode()
+        extra = lib.bl_last_error().decode() if status == 6 else ""
+        super().__init__(f"{where}: status {status} ({msg}){': ' + extra if extra else ''}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "bl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bl_last_error": (ctypes.c_char_p, []),
+    "bl_version": (ctypes.c_int, []),
+    "bl_ternary_packed_bytes": (_SZ, [_I64, _I64]),
+    "bl_sign_packed_bytes": (_SZ, [_I64, _I64]),
+    "bl_act_planes_bytes": (_SZ, [_I64, _I64]),
+    "bl_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "bl_workspace_clear": (ctypes.c_int, [_P, _SZ, _P]),
+    "bl_ternarize_absmean": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "bl_pack_ternary": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "bl_unpack_ternary": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "bl_pack_sign": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "bl_unpack_sign": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "bl_quant_act_int8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "bl_bitlinear_gemv": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "bl_bitlinear_gemm": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "bl_bitlinear_acc_i32": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
+    "bl_bitlinear_forward": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
+    "bl_onebit_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+}
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/libbitlinear.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bl_[a-z0-9_]+)\s*\(", text)))
+
+
+def load_library(path: str = LIB_PATH):
+    """dlopen libbitlinear.so and attach the C signatures. Raises if it is not built."""
+    if not os.path.exists(path):
+        raise ImportError(f"libbitlinear is not built ({path} missing); run "
+                          "`python -m ternary_weight_linear_amd.build` or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise BitLinearError(status, where, _lib)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {devs}")
+    d = devs.pop()
+    if d.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {d}")
+    return d
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _half_bits(t, name):
+    _need(t, torch.float16, name)
+    return t
+
+
+# ------------------------------------------------------------------------------------------
+# workspace: one zero-filled buffer per device, grown on demand, kept zero by the library
+# ------------------------------------------------------------------------------------------
+_ws_lock = threading.Lock()
+_ws = {}
+
+
+def workspace(device, nbytes: int):
+    """A zero-filled device buffer of at least nbytes for `device` (cached, grown on demand).
+    Calls that share it must be ordered on one stream, as the C contract requires."""
+    device = torch.device(device)
+    with _ws_lock:
+        buf = _ws.get(device)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _ws[device] = buf
+        return buf
+
+
+def _ws_for(device, M, N, K):
+    nbytes = _lib.bl_workspace_bytes(M, N, K)
+    if nbytes == 0:
+        raise ValueError(f"invalid shape M={M} N={N} K={K}")
+    buf = workspace(device, nbytes)
+    return buf, buf.numel()
+
+
+# ------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------
+def bl_ternary_packed_bytes(N: int, K: int) -> int:
+    return _lib.bl_ternary_packed_bytes(N, K)
+
+
+def bl_sign_packed_bytes(N: int, K: int) -> int:
+    return _lib.bl_sign_packed_bytes(N, K)
+
+
+def bl_act_planes_bytes(M: int, K: int) -> int:
+    return _lib.bl_act_planes_bytes(M, K)
+
+
+def bl_workspace_bytes(M: int, N: int, K: int) -> int:
+    return _lib.bl_workspace_bytes(M, N, K)
+
+
+def bl_ternarize_absmean(W, want_codes: bool = False):
+    """fp32 W [N, K] -> (packed uint8 [N*K/4], beta fp32 [1], codes int8 [N, K] or None)."""
+    _need(W, torch.float32, "W")
+    d = _dev(W)
+    N, K = W.shape
+    packed = torch.empty(max(_lib.bl_ternary_packed_bytes(N, K), 1), dtype=torch.uint8, device=d)
+    beta = torch.empty(1, dtype=torch.float32, device=d)
+    codes = torch.empty((N, K), dtype=torch.int8, device=d) if want_codes else None
+    ws, wsb = _ws_for(d, 1, N, K)
+    _check(_lib.bl_ternarize_absmean(_ptr(W), N, K, _ptr(codes), _ptr(packed), _ptr(beta),
+                                     _ptr(ws), wsb, _stream(d)), "bl_ternarize_absmean")
+    return packed, beta, codes
+
+
+def bl_pack_ternary(codes, n_invalid=None):
+    """int8 codes [N, K] -> uint8 T2-PN-64 [N*K/4]. n_invalid: optional int32 [1] counter."""
+    _need(codes, torch.int8, "codes")
+    d = _dev(codes, n_invalid)
+    N, K = codes.shape
+    out = torch.empty(max(_lib.bl_ternary_packed_bytes(N, K), 1), dtype=torch.uint8, device=d)
+    _check(_lib.bl_pack_ternary(_ptr(codes), N, K, _ptr(out), _ptr(n_invalid), _stream(d)),
+           "bl_pack_ternary")
+    return out
+
+
+def bl_unpack_ternary(packed, N: int, K: int, n_invalid=None):
+    _need(packed, torch.uint8, "packed")
+    d = _dev(packed, n_invalid)
+    out = torch.empty((N, K), dtype=torch.int8, device=d)
+    _check(_lib.bl_unpack_ternary(_ptr(packed), N, K, _ptr(out), _ptr(n_invalid), _stream(d)),
+           "bl_unpack_ternary")
+    return out
+
+
+def bl_pack_sign(W):
+    """fp32 W [N, K] -> uint8 S1-128 [N*K/8] (bit set iff W < 0)."""
+    _need(W, torch.float32, "W")
+    d = _dev(W)
+    N, K = W.shape
+    out = torch.empty(max(_lib.bl_sign_packed_bytes(N, K), 1), dtype=torch.uint8, device=d)
+    _check(_lib.bl_pack_sign(_ptr(W), N, K, _ptr(out), _stream(d)), "bl_pack_sign")
+    return out
+
+
+def bl_unpack_sign(packed, N: int, K: int):
+    _need(packed, torch.uint8, "packed")
+    d = _dev(packed)
+    out = torch.empty((N, K), dtype=torch.int8, device=d)
+    _check(_lib.bl_unpack_sign(_ptr(packed), N, K, _ptr(out), _stream(d)), "bl_unpack_sign")
+    return out
+
+
+def bl_quant_act_int8(x, want_q: bool = True, want_rowsum: bool = True, want_planes: bool = True):
+    """fp16 x [M, K] -> (q int8 [M, K] | None, gamma fp32 [M], rowsum int32 [M] | None,
+    planes uint32 [M, K/64, 16] | None)."""
+    _half_bits(x, "x")
+    d = _dev(x)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=d) if want_q else None
+    gamma = torch.empty(M, dtype=torch.float32, device=d)
+    rowsum = torch.empty(M, dtype=torch.int32, device=d) if want_rowsum else None
+    planes = torch.empty((M, K // 64, 16), dtype=torch.int32, device=d) if want_planes else None
+    _check(_lib.bl_quant_act_int8(_ptr(x), M, K, _ptr(q), _ptr(gamma), _ptr(rowsum), _ptr(planes),
+                                  _stream(d)), "bl_quant_act_int8")
+    return q, gamma, rowsum, planes
+
+
+def _beta_len(beta, N):
+    _need(beta, torch.float32, "beta")
+    return beta.numel()
+
+
+def bl_bitlinear_gemv(planes, gamma, wpacked, beta, N: int, K: int, out=None):
+    """Add-only GEMV (M <= 4): y fp32 [M, N]."""
+    _need(planes, torch.int32, "planes")
+    _need(gamma, torch.float32, "gamma")
+    _need(wpacked, torch.uint8, "wpacked")
+    d = _dev(planes, gamma, wpacked, beta)
+    M = gamma.numel()
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_gemv(_ptr(planes), _ptr(gamma), M, K, _ptr(wpacked), _ptr(beta),
+                                  _beta_len(beta, N), N, _ptr(y), _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_gemv")
+    return y
+
+
+def bl_bitlinear_gemm(q, gamma, wpacked, beta, N: int, out=None):
+    """int8-MFMA GEMM: y fp32 [M, N]."""
+    _need(q, torch.int8, "q")
+    _need(gamma, torch.float32, "gamma")
+    _need(wpacked, torch.uint8, "wpacked")
+    d = _dev(q, gamma, wpacked, beta)
+    M, K = q.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_gemm(_ptr(q), _ptr(gamma), M, K, _ptr(wpacked), _ptr(beta),
+                                  _beta_len(beta, N), N, _ptr(y), _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_gemm")
+    return y
+
+
+def bl_bitlinear_acc_i32(wpacked, N: int, K: int, q=None, planes=None, M: int | None = None,
+                         path: int = BL_PATH_AUTO):
+    """Raw int32 accumulators [M, N] of the chosen kernel path."""
+    _need(wpacked, torch.uint8, "wpacked")
+    if q is not None:
+        _need(q, torch.int8, "q")
+    if planes is not None:
+        _need(planes, torch.int32, "planes")
+    d = _dev(wpacked, q, planes)
+    if M is None:
+        M = q.shape[0] if q is not None else planes.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_acc_i32(_ptr(q), _ptr(planes), M, K, _ptr(wpacked), N, _ptr(acc), path,
+                                     _ptr(ws), wsb, _stream(d)), "bl_bitlinear_acc_i32")
+    return acc
+
+
+def bl_bitlinear_forward(x, wpacked, beta, N: int, path: int = BL_PATH_AUTO, out=None):
+    """fp16 x [M, K] -> y fp32 [M, N]: quantise + GEMV/GEMM + rescale."""
+    _half_bits(x, "x")
+    _need(wpacked, torch.uint8, "wpacked")
+    d = _dev(x, wpacked, beta)
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_forward(_ptr(x), M, K, _ptr(wpacked), _ptr(beta), _beta_len(beta, N),
+                                     N, _ptr(y), path, _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_forward")
+    return y
+
+
+def bl_onebit_linear(x, g, spacked, h, out=None):
+    """OneBit layer: fp16 x [M, K], g fp16 [K], S1-128 signs, h fp16 [N] -> y fp32 [M, N]."""
+    _half_bits(x, "x")
+    _half_bits(g, "g")
+    _half_bits(h, "h")
+    _need(spacked, torch.uint8, "spacked")
+    d = _dev(x, g, spacked, h)
+    M, K = x.shape
+    N = h.numel()
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_onebit_linear(_ptr(x), _ptr(g), _ptr(spacked), _ptr(h), M, N, K, _ptr(y),
+                                 _ptr(ws), wsb, _stream(d)), "bl_onebit_linear")
+    return y
+
+
+__all__ = [n for n in list(globals()) if n.startswith("bl_")] + [
+    "BitLinearError", "workspace", "load_library", "header_functions", "LIB_PATH",
+    "BL_PATH_AUTO", "BL_PATH_GEMV", "BL_PATH_GEMM"]

@@ -1,0 +1,349 @@
+// The C ABI of libbitlinear: host-side argument checks, workspace carve-up and dispatch.
+// Every check runs before anything is queued; see include/libbitlinear.h for the contract.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e),
+                static_cast<int>(e));
+  return BL_ERR_HIP;
+}
+
+inline int check_launch(hipError_t e, const char* where) {
+  return e == hipSuccess ? BL_OK : hip_fail(e, where);
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Half-open byte ranges [a, a + na) and [b, b + nb) intersect.
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+inline bool dims_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
+}
+
+}  // namespace
+
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes, size_t& o, size_t& b) {
+    o = off;
+    b = round256(bytes);
+    off += b;
+  };
+  take(static_cast<size_t>(kMaxCounters) * 4, L.cnt_off, L.cnt_bytes);
+  take(static_cast<size_t>(kAccCap) * 4, L.acc_off, L.acc_bytes);
+  const int64_t mr = std::min<int64_t>(M, 4);
+  const int64_t ks = (K % 128 == 0 && N % 64 == 0) ? onebit_splits(M, N, K) : 1;
+  take(static_cast<size_t>(ks) * mr * N * 4, L.part_off, L.part_bytes);
+  take(static_cast<size_t>(kAbsmeanBlocks) * kAbsmeanBins * 8, L.bins_off, L.bins_bytes);
+  take(static_cast<size_t>(M) * K, L.q_off, L.q_bytes);
+  take(static_cast<size_t>(M) * K, L.planes_off, L.planes_bytes);
+  take(static_cast<size_t>(M) * 4, L.gamma_off, L.gamma_bytes);
+  L.total = off;
+  return L;
+}
+
+}  // namespace bl
+
+using namespace bl;
+
+namespace {
+
+// Common checks of the ternary product entry points. Returns BL_OK or a status.
+int check_ternary_product(int64_t M, int64_t K, const void* wpacked, int64_t N,
+                          const float* gamma, void* ws, size_t ws_bytes) {
+  if (!wpacked || !gamma) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || 127 * K >= (int64_t(1) << 31)) return BL_ERR_SHAPE;
+  if (!aligned16(wpacked)) return BL_ERR_ALIGN;
+  if (!ws || ws_bytes < ws_layout(M, N, K).total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  return BL_OK;
+}
+
+int check_beta(const float* beta, int64_t beta_len, int64_t N) {
+  if (!beta) return BL_ERR_NULL;
+  if (beta_len != 1 && beta_len != N) return BL_ERR_ARG;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bl_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "a required pointer is NULL";
+    case BL_ERR_SHAPE: return "a size is out of range or not a multiple its layout needs";
+    case BL_ERR_ALIGN: return "a pointer lacks the alignment its loads need";
+    case BL_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    case BL_ERR_WORKSPACE: return "workspace missing or smaller than bl_workspace_bytes()";
+    case BL_ERR_HIP: return "a HIP call failed (see bl_last_error)";
+    case BL_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* bl_last_error(void) { return g_last_error; }
+
+int bl_version(void) { return 10000; }
+
+size_t bl_ternary_packed_bytes(int64_t N, int64_t K) {
+  if (!dims_ok(1, N, K) || N % 64 || K % 64) return 0;
+  return static_cast<size_t>(N) * K / 4;
+}
+
+size_t bl_sign_packed_bytes(int64_t N, int64_t K) {
+  if (!dims_ok(1, N, K) || N % 64 || K % 128) return 0;
+  return static_cast<size_t>(N) * K / 8;
+}
+
+size_t bl_act_planes_bytes(int64_t M, int64_t K) {
+  if (!dims_ok(M, 1, K) || K % 64) return 0;
+  return static_cast<size_t>(M) * K;
+}
+
+size_t bl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!dims_ok(M, N, K)) return 0;
+  return ws_layout(M, N, K).total;
+}
+
+int bl_workspace_clear(void* ws, size_t bytes, void* stream) {
+  if (!ws) return BL_ERR_NULL;
+  return check_launch(launch_fill_zero(ws, bytes, static_cast<hipStream_t>(stream)),
+                      "bl_workspace_clear");
+}
+
+int bl_ternarize_absmean(const float* W, int64_t N, int64_t K, int8_t* codes, void* packed,
+                         float* beta, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !beta || (!codes && !packed)) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 64 || N * K >= (int64_t(1) << 32)) return BL_ERR_SHAPE;
+  if (!aligned16(W) || (codes && !aligned16(codes)) || (packed && !aligned16(packed)))
+    return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(1, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  const size_t wb = static_cast<size_t>(N) * K * 4;
+  if (overlap(codes, N * K, W, wb) || overlap(packed, N * K / 4, W, wb) ||
+      overlap(codes, N * K, packed, N * K / 4) || overlap(beta, 4, W, wb) ||
+      overlap(beta, 4, codes, N * K) || overlap(beta, 4, packed, N * K / 4))
+    return BL_ERR_ALIAS;
+  auto* bins = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + L.bins_off);
+  return check_launch(launch_ternarize_absmean(W, N, K, codes, packed, beta, bins,
+                                               static_cast<hipStream_t>(stream)),
+                      "bl_ternarize_absmean");
+}
+
+int bl_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* packed, int32_t* n_invalid,
+                    void* stream) {
+  if (!codes || !packed) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 64) return BL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(packed)) return BL_ERR_ALIGN;
+  if (overlap(codes, N * K, packed, N * K / 4) || overlap(n_invalid, 4, packed, N * K / 4))
+    return BL_ERR_ALIAS;
+  return check_launch(launch_pack_ternary(codes, N, K, packed, n_invalid,
+                                          static_cast<hipStream_t>(stream)),
+                      "bl_pack_ternary");
+}
+
+int bl_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes, int32_t* n_invalid,
+                      void* stream) {
+  if (!codes || !packed) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 64) return BL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(packed)) return BL_ERR_ALIGN;
+  if (overlap(codes, N * K, packed, N * K / 4) || overlap(n_invalid, 4, codes, N * K))
+    return BL_ERR_ALIAS;
+  return check_launch(launch_unpack_ternary(packed, N, K, codes, n_invalid,
+                                            static_cast<hipStream_t>(stream)),
+                      "bl_unpack_ternary");
+}
+
+int bl_pack_sign(const float* W, int64_t N, int64_t K, void* packed, void* stream) {
+  if (!W || !packed) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(packed)) return BL_ERR_ALIGN;
+  if (overlap(W, static_cast<size_t>(N) * K * 4, packed, N * K / 8)) return BL_ERR_ALIAS;
+  return check_launch(launch_pack_sign(W, N, K, packed, static_cast<hipStream_t>(stream)),
+                      "bl_pack_sign");
+}
+
+int bl_unpack_sign(const void* packed, int64_t N, int64_t K, int8_t* signs, void* stream) {
+  if (!signs || !packed) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
+  if (!aligned16(signs) || !aligned16(packed)) return BL_ERR_ALIGN;
+  if (overlap(signs, N * K, packed, N * K / 8)) return BL_ERR_ALIAS;
+  return check_launch(launch_unpack_sign(packed, N, K, signs, static_cast<hipStream_t>(stream)),
+                      "bl_unpack_sign");
+}
+
+int bl_quant_act_int8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* gamma,
+                      int32_t* rowsum, uint32_t* planes, void* stream) {
+  if (!x || !gamma || (!q && !planes)) return BL_ERR_NULL;
+  if (!dims_ok(M, 1, K) || K % 64 || K > 28672 || M > (int64_t(1) << 24)) return BL_ERR_SHAPE;
+  if (!aligned16(x) || (q && !aligned16(q)) || (planes && !aligned16(planes))) return BL_ERR_ALIGN;
+  const size_t xb = static_cast<size_t>(M) * K * 2, qb = static_cast<size_t>(M) * K;
+  const void* outs[4] = {q, gamma, rowsum, planes};
+  const size_t outb[4] = {qb, static_cast<size_t>(M) * 4, static_cast<size_t>(M) * 4, qb};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], x, xb)) return BL_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return BL_ERR_ALIAS;
+  }
+  return check_launch(launch_quant_act(x, M, K, q, gamma, rowsum, planes,
+                                       static_cast<hipStream_t>(stream)),
+                      "bl_quant_act_int8");
+}
+
+int bl_bitlinear_gemv(const uint32_t* planes, const float* gamma, int64_t M, int64_t K,
+                      const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                      float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!planes || !y) return BL_ERR_NULL;
+  if (M > 4) return BL_ERR_SHAPE;
+  int st = check_ternary_product(M, K, wpacked, N, gamma, ws, ws_bytes);
+  if (st) return st;
+  if ((st = check_beta(beta, beta_len, N))) return st;
+  if (!aligned16(planes)) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, planes, M * K) || overlap(y, yb, wpacked, N * K / 4) ||
+      overlap(y, yb, gamma, M * 4) || overlap(y, yb, beta, beta_len * 4) ||
+      overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  const WsLayout L = ws_layout(M, N, K);
+  char* w = static_cast<char*>(ws);
+  return check_launch(launch_gemv(planes, gamma, static_cast<int>(M), K, wpacked, beta, beta_len,
+                                  N, y, nullptr, reinterpret_cast<int32_t*>(w + L.acc_off),
+                                  reinterpret_cast<uint32_t*>(w + L.cnt_off),
+                                  static_cast<hipStream_t>(stream)),
+                      "bl_bitlinear_gemv");
+}
+
+int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                      const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                      float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !y) return BL_ERR_NULL;
+  int st = check_ternary_product(M, K, wpacked, N, gamma, ws, ws_bytes);
+  if (st) return st;
+  if ((st = check_beta(beta, beta_len, N))) return st;
+  if (!aligned16(q)) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, q, M * K) || overlap(y, yb, wpacked, N * K / 4) ||
+      overlap(y, yb, gamma, M * 4) || overlap(y, yb, beta, beta_len * 4) ||
+      overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  const WsLayout L = ws_layout(M, N, K);
+  char* w = static_cast<char*>(ws);
+  return check_launch(launch_gemm(q, gamma, M, K, wpacked, beta, beta_len, N, y, nullptr,
+                                  reinterpret_cast<int32_t*>(w + L.acc_off),
+                                  reinterpret_cast<uint32_t*>(w + L.cnt_off),
+                                  static_cast<hipStream_t>(stream)),
+                      "bl_bitlinear_gemm");
+}
+
+int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int64_t K,
+                         const void* wpacked, int64_t N, int32_t* acc, int path, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!acc || !wpacked) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || 127 * K >= (int64_t(1) << 31)) return BL_ERR_SHAPE;
+  if (path == BL_PATH_AUTO) path = (M <= 2 && planes) ? BL_PATH_GEMV : BL_PATH_GEMM;
+  if (path != BL_PATH_GEMV && path != BL_PATH_GEMM) return BL_ERR_ARG;
+  if (path == BL_PATH_GEMV && !planes) return BL_ERR_NULL;
+  if (path == BL_PATH_GEMM && !q) return BL_ERR_NULL;
+  if (path == BL_PATH_GEMV && M > 4) return BL_ERR_SHAPE;
+  if (!aligned16(wpacked) || (q && !aligned16(q)) || (planes && !aligned16(planes)))
+    return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t ab = static_cast<size_t>(M) * N * 4;
+  if (overlap(acc, ab, q, M * K) || overlap(acc, ab, planes, M * K) ||
+      overlap(acc, ab, wpacked, N * K / 4) || overlap(acc, ab, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  auto* wsacc = reinterpret_cast<int32_t*>(w + L.acc_off);
+  auto* wscnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (path == BL_PATH_GEMV)
+    return check_launch(launch_gemv(planes, nullptr, static_cast<int>(M), K, wpacked, nullptr, 1,
+                                    N, nullptr, acc, wsacc, wscnt, s),
+                        "bl_bitlinear_acc_i32");
+  return check_launch(launch_gemm(q, nullptr, M, K, wpacked, nullptr, 1, N, nullptr, acc, wsacc,
+                                  wscnt, s),
+                      "bl_bitlinear_acc_i32");
+}
+
+int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
+                         const float* beta, int64_t beta_len, int64_t N, float* y, int path,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !y || !wpacked) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || K > 28672) return BL_ERR_SHAPE;
+  int st = check_beta(beta, beta_len, N);
+  if (st) return st;
+  if (path == BL_PATH_AUTO) path = M <= 2 ? BL_PATH_GEMV : BL_PATH_GEMM;
+  if (path != BL_PATH_GEMV && path != BL_PATH_GEMM) return BL_ERR_ARG;
+  if (path == BL_PATH_GEMV && M > 4) return BL_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(wpacked)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, wpacked, N * K / 4) ||
+      overlap(y, yb, beta, beta_len * 4) || overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  auto* qbuf = reinterpret_cast<int8_t*>(w + L.q_off);
+  auto* pbuf = reinterpret_cast<uint32_t*>(w + L.planes_off);
+  auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_quant_act(x, M, K, path == BL_PATH_GEMM ? qbuf : nullptr, gbuf, nullptr,
+                                  path == BL_PATH_GEMV ? pbuf : nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward (quantise)");
+  if (path == BL_PATH_GEMV)
+    e = launch_gemv(pbuf, gbuf, static_cast<int>(M), K, wpacked, beta, beta_len, N, y, nullptr,
+                    reinterpret_cast<int32_t*>(w + L.acc_off),
+                    reinterpret_cast<uint32_t*>(w + L.cnt_off), s);
+  else
+    e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr,
+                    reinterpret_cast<int32_t*>(w + L.acc_off),
+                    reinterpret_cast<uint32_t*>(w + L.cnt_off), s);
+  return check_launch(e, "bl_bitlinear_forward");
+}
+
+int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked, const uint16_t* h,
+                     int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!x || !g || !spacked || !h || !y) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
+  if (!aligned16(spacked)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, g, K * 2) || overlap(y, yb, h, N * 2) ||
+      overlap(y, yb, spacked, N * K / 8) || overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  return check_launch(launch_onebit(x, g, spacked, h, M, N, K, y,
+                                    reinterpret_cast<float*>(w + L.part_off),
+                                    reinterpret_cast<uint32_t*>(w + L.cnt_off),
+                                    static_cast<hipStream_t>(stream)),
+                      "bl_onebit_linear");
+}
+
+}  // extern "C"

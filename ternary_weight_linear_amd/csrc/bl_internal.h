@@ -1,0 +1,75 @@
+// Internal declarations shared by the libbitlinear translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "libbitlinear.h"
+
+namespace bl {
+
+constexpr int kQb = 127;               // activation range [-127, 127]
+constexpr int kAbsmeanBlocks = 1024;   // partial histograms of the exact absmean sum
+constexpr int kAbsmeanBins = 256;      // one bin per fp32 exponent field value
+
+// Carve-up of the caller's workspace. Every region starts 256-byte aligned.
+// cnt and acc sit at fixed offsets for every shape, must be zero on entry and are left
+// zero by every call; the regions after them are scratch that any call may overwrite.
+// Fixed positions keep one shape's scratch from ever landing on another shape's
+// zero-maintained region when a workspace is shared.
+constexpr int64_t kMaxCounters = 65536;          // completion counters (256 KiB)
+constexpr int64_t kAccCap = int64_t(64) * 65536; // int32 split-K accumulators (16 MiB)
+struct WsLayout {
+  size_t cnt_off, cnt_bytes;       // uint32 completion counters, one per output tile
+  size_t acc_off, acc_bytes;       // int32 [M, N] split-K accumulators
+  size_t part_off, part_bytes;     // fp32 [KS, M, N] split-K partial sums (OneBit)
+  size_t bins_off, bins_bytes;     // uint64 [kAbsmeanBlocks, 256] + flag (absmean)
+  size_t q_off, q_bytes;           // int8 [M, K] activations (forward)
+  size_t planes_off, planes_bytes; // X8-64 planes [M*K bytes] (forward)
+  size_t gamma_off, gamma_bytes;   // fp32 [M] (forward)
+  size_t total;
+};
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
+
+// Split-K factor of the OneBit kernels for a shape (fixes the workspace size).
+int onebit_splits(int64_t M, int64_t N, int64_t K);
+// Number of output tiles (completion counters) the GEMM uses for a shape.
+int64_t gemm_max_tiles(int64_t M, int64_t N);
+
+// ---- launchers (all asynchronous on `s`) -----------------------------------------------
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+hipError_t launch_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* packed,
+                               int32_t* n_invalid, hipStream_t s);
+hipError_t launch_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes,
+                                 int32_t* n_invalid, hipStream_t s);
+hipError_t launch_pack_sign(const float* W, int64_t N, int64_t K, void* packed, hipStream_t s);
+hipError_t launch_unpack_sign(const void* packed, int64_t N, int64_t K, int8_t* signs,
+                              hipStream_t s);
+hipError_t launch_ternarize_absmean(const float* W, int64_t N, int64_t K, int8_t* codes,
+                                    void* packed, float* beta, unsigned long long* bins,
+                                    hipStream_t s);
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* gamma,
+                            int32_t* rowsum, uint32_t* planes, hipStream_t s);
+
+// y != nullptr: fp32 epilogue into y; acc_out != nullptr: raw int32 accumulators.
+hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_t K,
+                       const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       hipStream_t s);
+hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                       const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       hipStream_t s);
+hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
+                         const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
+                         float* ws_part, uint32_t* ws_cnt, hipStream_t s);
+
+// ---- device helpers ---------------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+}  // namespace bl

@@ -1,0 +1,193 @@
+// Batched / prefill GEMM for ternary weights on int8 matrix cores.
+//
+// [b158] "实验及结果": b1.58 models serve large batches (Table 3, sequence length 512) and
+// the matrix product is an int8 accumulation (Fig. 3). Here the packed T2-PN-64 weights
+// are expanded to int8 {-1, 0, +1} tiles in LDS and multiplied with the int8 activations
+// by v_mfma_i32_16x16x64_i8 with int32 accumulation, then rescaled in a fused epilogue.
+//
+// Expansion: for a 32-input word, (X >> j) & 0x01010101 puts the flags of inputs 4j..4j+3
+// in bytes 0..3 (the layout's bit order was chosen for this), and
+// (P_bytes) + 255 * (N_bytes) turns flags into int8 +1 / -1 bytes in one v_mad_u32_u24.
+//
+// Work split: a 256-thread workgroup owns a BM x BN output tile (4 waves, each a
+// (BM/WGM) x (BN/WGN) sub-tile of 16 x 16 MFMA fragments) and a range of 64-input k tiles.
+// Small-M shapes split K across workgroups; partial accumulators then meet in int32
+// atomics in the workspace and the last workgroup of a tile applies the epilogue.
+// Workgroup ids are remapped so that tiles sharing a weight column block run on the same
+// XCD (ids are dealt round-robin to the 8 XCDs), keeping that block in one L2.
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLd = 64 + 16;   // LDS row pitch in bytes (64 k per tile + pad)
+
+template <int BM, int BN, int WGM>
+__global__ __launch_bounds__(256) void gemm_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ gamma, int64_t M, int64_t K,
+    const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
+    float* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
+    uint32_t* __restrict__ ws_cnt, int tiles_per_split, int MT, int NT) {
+  constexpr int WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  static_assert(FM >= 1 && FN >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) int8_t As[BM * kLd];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[BN * kLd];
+  __shared__ uint32_t last_flag;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // XCD-aware tile order: blocks b, b+8, b+16, ... run on one XCD; give them consecutive
+  // logical tiles, which share a weight column block (m varies fastest).
+  const int nblocks = MT * NT;
+  int L = blockIdx.x;
+  if ((nblocks & 7) == 0) L = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
+  const int mt = L % MT, nt = L / MT;
+  const int64_t m0 = static_cast<int64_t>(mt) * BM, n0 = static_cast<int64_t>(nt) * BN;
+  const int KT = static_cast<int>(K / 64);
+  const int t0 = blockIdx.y * tiles_per_split;
+  const int t1 = min(KT, t0 + tiles_per_split);
+
+  i32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+
+  for (int tk = t0; tk < t1; ++tk) {
+    // activations: BM rows x 64 bytes
+    for (int c = tid; c < BM * 4; c += 256) {
+      const int r = c >> 2, part = c & 3;
+      const int64_t row = m0 + r;
+      u32x4 v = {0, 0, 0, 0};
+      if (row < M) v = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + part * 16);
+      *reinterpret_cast<u32x4*>(As + r * kLd + part * 16) = v;
+    }
+    // weights: BN rows x 2 halves of 32 inputs, expanded to int8
+    for (int c = tid; c < BN * 2; c += 256) {
+      const int r = c >> 1, hh = c & 1;
+      const int64_t n = n0 + r;
+      uint32_t o[8];
+      if (n < N) {
+        const u32x4 w = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
+        const uint32_t P = hh ? w.y : w.x, Nm = hh ? w.w : w.z;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pb = (P >> j) & 0x01010101u, nb = (Nm >> j) & 0x01010101u;
+          o[j] = pb + nb * 255u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = 0;
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(Bs + r * kLd + hh * 32);
+      dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+      dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+    }
+    __syncthreads();
+    i32x4 a[FM], b[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const i32x4*>(As + (wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const i32x4*>(Bs + (wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    __syncthreads();
+  }
+
+  // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r (r = 0..3), column l % 16.
+  const bool split = gridDim.y > 1;
+  if (split) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
+          const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
+          if (row < M && col < N) atomicAdd(&ws_acc[row * N + col], acc[i][j][r]);
+        }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last_flag = (atomicAdd(&ws_cnt[L], 1u) == gridDim.y - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
+        const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
+        if (row < M && col < N) {
+          int v = acc[i][j][r];
+          if (split) v = atomicExch(&ws_acc[row * N + col], 0);
+          if (acc_out) acc_out[row * N + col] = v;
+          if (y) {
+            const float scale = gamma[row] / 127.0f;
+            y[row * N + col] = static_cast<float>(v) * scale * beta[beta_len == 1 ? 0 : col];
+          }
+        }
+      }
+  if (split && tid == 0) atomicExch(&ws_cnt[L], 0u);
+}
+
+template <int BM, int BN, int WGM>
+hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                       const u32x4* W, const float* beta, int64_t beta_len, int64_t N, float* y,
+                       int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
+  const int MT = static_cast<int>((M + BM - 1) / BM), NT = static_cast<int>((N + BN - 1) / BN);
+  const int KT = static_cast<int>(K / 64);
+  const int64_t tiles = static_cast<int64_t>(MT) * NT;
+  int nsplit = 1;
+  if (M <= 64) {   // HBM-bound shapes: fill the chip by splitting K (cheap: M x N atomics)
+    nsplit = static_cast<int>(std::min<int64_t>((1024 + tiles - 1) / tiles, std::max(1, KT / 8)));
+    nsplit = std::max(nsplit, 1);
+  }
+  if (M * N > kAccCap || tiles > kMaxCounters) nsplit = 1;
+  const int tps = (KT + nsplit - 1) / nsplit;
+  nsplit = (KT + tps - 1) / tps;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM>), dim3(static_cast<unsigned>(tiles), nsplit),
+                     dim3(256), 0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,
+                     ws_cnt, tps, MT, NT);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                       const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       hipStream_t s) {
+  const u32x4* W = static_cast<const u32x4*>(wpacked);
+  if (M <= 16)
+    return launch_tile<16, 128, 1>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
+  if (M <= 32)
+    return launch_tile<32, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
+  if (M <= 64)
+    return launch_tile<64, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
+  return launch_tile<128, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
+}
+
+int64_t gemm_max_tiles(int64_t M, int64_t N) {
+  const int64_t bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  return ((M + bm - 1) / bm) * ((N + 127) / 128);
+}
+
+}  // namespace bl

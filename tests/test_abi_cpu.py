@@ -1,0 +1,103 @@
+"""The C ABI without a GPU: the library loads, exports every function the header declares,
+and its host-side checks return the documented status before anything is queued.
+
+The pointers passed here are fake addresses; every call below fails a host check, so no
+HIP call is ever made with them."""
+import ctypes
+
+import pytest
+
+from ternary_weight_linear_amd.build import LIB_PATH
+
+OK, NULL, SHAPE, ALIGN, ALIAS, WS, HIP, ARG = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import ternary_weight_linear_amd as tw
+    return tw.load_library(LIB_PATH)
+
+
+def test_exports_every_header_function(lib):
+    import ternary_weight_linear_amd as tw
+    names = tw.header_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/libbitlinear.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for s in range(8):
+        assert lib.bl_status_string(s)
+    assert lib.bl_status_string(99) == b"unknown status"
+    assert lib.bl_version() >= 10000
+    assert lib.bl_last_error() == b""
+
+
+def test_size_queries(lib):
+    assert lib.bl_ternary_packed_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert lib.bl_ternary_packed_bytes(28672, 8192) == 28672 * 8192 // 4
+    assert lib.bl_ternary_packed_bytes(100, 64) == 0          # N % 64
+    assert lib.bl_sign_packed_bytes(4096, 4096) == 2097152
+    assert lib.bl_sign_packed_bytes(64, 192) == 0             # K % 128
+    assert lib.bl_act_planes_bytes(3, 640) == 3 * 640
+    ws = lib.bl_workspace_bytes(512, 8640, 3200)
+    assert ws >= 512 * 8640 * 4 and ws % 256 == 0
+    assert lib.bl_workspace_bytes(0, 64, 64) == 0
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A = 0x100000          # fake, 256-aligned addresses far apart
+B = 0x40000000
+C = 0x80000000
+D = 0xC0000000
+
+
+def test_pack_checks(lib):
+    assert lib.bl_pack_ternary(None, 64, 64, _p(B), None, None) == NULL
+    assert lib.bl_pack_ternary(_p(A), 64, 96, _p(B), None, None) == SHAPE
+    assert lib.bl_pack_ternary(_p(A), 0, 64, _p(B), None, None) == SHAPE
+    assert lib.bl_pack_ternary(_p(A + 1), 64, 64, _p(B), None, None) == ALIGN
+    assert lib.bl_pack_ternary(_p(A), 64, 64, _p(A + 64), None, None) == ALIAS
+    assert lib.bl_pack_sign(_p(A), 64, 64, _p(B), None) == SHAPE
+    assert lib.bl_unpack_sign(_p(A), 64, 128, None, None) == NULL
+    assert lib.bl_unpack_ternary(_p(A), 64, 64, _p(A + 512), None, None) == ALIAS
+
+
+def test_quant_checks(lib):
+    assert lib.bl_quant_act_int8(_p(A), 2, 64, None, _p(C), None, None, None) == NULL
+    assert lib.bl_quant_act_int8(_p(A), 2, 100, _p(B), _p(C), None, None, None) == SHAPE
+    assert lib.bl_quant_act_int8(_p(A), 2, 64, _p(A + 128), _p(C), None, None, None) == ALIAS
+    assert lib.bl_quant_act_int8(_p(A), 2, 64, _p(B), _p(B + 64), None, None, None) == ALIAS
+
+
+def test_product_checks(lib):
+    M, N, K = 1, 128, 256
+    wsb = lib.bl_workspace_bytes(M, N, K)
+    ok = dict(planes=_p(A), gamma=_p(A + 65536), w=_p(B), beta=_p(B + 1 << 20), y=_p(C), ws=_p(D))
+    def gemv(**kw):
+        a = {**ok, **kw}
+        return lib.bl_bitlinear_gemv(a["planes"], a["gamma"], kw.get("M", M), K, a["w"], a["beta"],
+                                     kw.get("beta_len", 1), kw.get("N", N), a["y"], a["ws"],
+                                     kw.get("wsb", wsb), None)
+    assert gemv(planes=None) == NULL
+    assert gemv(N=100) == SHAPE
+    assert gemv(M=5) == SHAPE
+    assert gemv(beta_len=7) == ARG
+    assert gemv(wsb=16) == WS
+    assert gemv(ws=None) == WS
+    assert gemv(ws=_p(D + 16)) == ALIGN
+    assert gemv(w=_p(B + 4)) == ALIGN
+    assert gemv(y=_p(B + 64)) == ALIAS
+    assert lib.bl_bitlinear_acc_i32(_p(A), None, M, K, _p(B), N, _p(C), 9, _p(D), wsb, None) == ARG
+    assert lib.bl_bitlinear_acc_i32(None, None, M, K, _p(B), N, _p(C), 2, _p(D), wsb, None) == NULL
+    assert lib.bl_bitlinear_forward(_p(A), 1, 64, _p(B), _p(C), 1, 64, _p(C), 5, _p(D),
+                                    lib.bl_workspace_bytes(1, 64, 64), None) == ARG
+    assert lib.bl_onebit_linear(_p(A), _p(A + 4096), _p(B), _p(B + 8192), 1, 64, 192, _p(C), _p(D),
+                                1 << 20, None) == SHAPE
+    assert lib.bl_ternarize_absmean(_p(A), 64, 64, None, None, _p(C), _p(D), 1 << 24, None) == NULL
+    assert lib.bl_ternarize_absmean(_p(A), 1 << 17, 1 << 16, None, _p(B), _p(C), _p(D), 1 << 24,
+                                    None) == SHAPE

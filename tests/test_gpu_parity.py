@@ -1,0 +1,270 @@
+"""GPU parity: every libbitlinear entry point against the CPU oracle on the same seeded
+inputs. Integer results (packed bytes, codes, beta bits, int8 activations, bit planes,
+int32 accumulators) must match exactly; fp32 outputs within 1e-3 of the fp64 oracle
+(relative per element for b1.58; against |h| * sum|x g| for OneBit)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_weight_linear_amd as tw
+from tests.gpu_util import DEV, assert_rel, assert_scaled, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ----------------------------------------------------------------------------- packing
+@pytest.mark.parametrize("N,K", [(64, 64), (192, 320), (512, 512), (1024, 3200)])
+def test_pack_unpack_ternary(N, K):
+    say("pack_ternary", N, K)
+    codes = synth.ternary_codes(synth.matrix_key(0, 90, N, K), N, K)
+    codes[0, :5] = [1, -1, 0, 1, -1]
+    ref = oracle.pack_ternary(codes)
+    g = tw.bl_pack_ternary(dev(codes))
+    assert np.array_equal(host(g), ref)
+    back = tw.bl_unpack_ternary(g, N, K)
+    assert np.array_equal(host(back), codes)
+
+
+def test_pack_ternary_invalid_codes():
+    say("pack_ternary invalid")
+    codes = np.zeros((64, 128), np.int8)
+    codes[3, 7] = 5
+    codes[9, 100] = -2
+    codes[10, 0] = 1
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    g = tw.bl_pack_ternary(dev(codes), n_invalid=cnt)
+    ref, bad = oracle.pack_ternary(codes, count_invalid=True)
+    assert np.array_equal(host(g), ref) and int(host(cnt)[0]) == bad == 2
+    gb = g.clone()
+    gb[0] |= 1
+    gb[8] |= 1                                           # (P, N) = (1, 1) at (0, 0)
+    cnt.zero_()
+    back = tw.bl_unpack_ternary(gb, 64, 128, n_invalid=cnt)
+    ref_codes, ref_bad = oracle.unpack_ternary(host(gb), 64, 128, count_invalid=True)
+    assert np.array_equal(host(back), ref_codes) and int(host(cnt)[0]) == ref_bad == 1
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (192, 256), (512, 512), (4096, 4096)])
+def test_pack_unpack_sign(N, K):
+    say("pack_sign", N, K)
+    W = synth.normal_fp32((N, K), 0, 91, N, K)
+    W[0, :4] = [0.0, -0.0, np.nan, -np.inf]
+    ref = oracle.pack_sign(W)
+    g = tw.bl_pack_sign(dev(W))
+    assert np.array_equal(host(g), ref)
+    assert np.array_equal(host(tw.bl_unpack_sign(g, N, K)), oracle.unpack_sign(ref, N, K))
+    if (N, K) == (4096, 4096):
+        # the storage count of the OneBit page, from the bytes the GPU packer produced
+        assert 8 * g.numel() + 16 * (N + K) == 16908288
+
+
+# ----------------------------------------------------------------------------- absmean
+def _ternarize_case(W):
+    packed, beta, codes = tw.bl_ternarize_absmean(dev(W), want_codes=True)
+    rc, rb = oracle.ternarize_absmean(W)
+    gb = host(beta)
+    if np.isnan(rb):
+        assert np.isnan(gb[0])
+    else:
+        assert gb.view(np.uint32)[0] == np.float32(rb).view(np.uint32)
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(packed), oracle.pack_ternary(rc))
+
+
+@pytest.mark.parametrize("N,K,std", [(512, 512, 0.02), (192, 320, 1.0), (3200, 3200, 0.02)])
+def test_ternarize_absmean(N, K, std):
+    say("ternarize_absmean", N, K, std)
+    W = synth.normal_fp32((N, K), 0, 1, N, K, std=std)
+    _ternarize_case(W)
+
+
+def test_ternarize_absmean_edge_cases():
+    say("ternarize_absmean edge")
+    _ternarize_case(np.zeros((64, 64), np.float32))
+    W = synth.normal_fp32((64, 128), 0, 92, 1)
+    W[5, 5] = np.nan
+    _ternarize_case(W)
+    W = np.tile(np.array([0.5, 1.5, 1.0, 1.0], np.float32), (64, 16))      # exact tie at 0.5
+    _ternarize_case(W)
+    rg = synth.rng(0, 93)
+    W = (rg.standard_normal((128, 192)) * np.exp2(rg.integers(-149, 30, (128, 192)))).astype(np.float32)
+    _ternarize_case(W)                                                       # wide exponents, subnormals
+
+
+# ----------------------------------------------------------------------------- quantiser
+def _quant_case(x):
+    M, K = x.shape
+    q, gamma, rowsum, planes = tw.bl_quant_act_int8(dev(x))
+    rq, rg, rr = oracle.quant_act_int8(x)
+    gg = host(gamma)
+    assert np.array_equal(np.isnan(gg), np.isnan(rg))
+    assert np.array_equal(gg[~np.isnan(rg)].view(np.uint32), rg[~np.isnan(rg)].view(np.uint32))
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(rowsum), rr)
+    assert np.array_equal(host(planes).view(np.uint32).reshape(M, K // 64, 16), oracle.act_planes(rq))
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (8, 512), (3, 640), (1, 8192), (4, 28672), (512, 3200)])
+def test_quant_act(M, K):
+    say("quant_act", M, K)
+    x = synth.normal_fp16((M, K), 0, 2, M, K)
+    if M == 512:
+        x, _ = synth.with_outlier_channels(x, 0.01, 20.0, 0, 3, K)
+    _quant_case(x)
+
+
+def test_quant_act_degenerate_rows():
+    say("quant_act degenerate")
+    x = synth.normal_fp16((5, 128), 0, 94, 0)
+    x[1] = 0
+    x[2, 17] = np.float16(np.inf)
+    x[3, 100] = np.float16(np.nan)
+    x[4, :] = np.float16(-65504)
+    _quant_case(x)
+
+
+def test_quant_act_exhaustive_fp16():
+    """Every finite fp16 x against a ladder of gamma values: rows [x, gamma, 0, ...]."""
+    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite = all16[np.isfinite(all16)]
+    for gamma in [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
+                  np.float16(3.14), np.float16(127.0)]:
+        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
+        say("quant exhaustive gamma", gamma, xs.size)
+        x = np.zeros((xs.size, 64), np.float16)
+        x[:, 0] = xs
+        x[:, 1] = gamma
+        _quant_case(x)
+
+
+# ----------------------------------------------------------------------------- products
+def _weights(N, K, seed=0):
+    codes = synth.ternary_codes(synth.matrix_key(seed, 95, N, K), N, K)
+    return codes, tw.bl_pack_ternary(dev(codes))
+
+
+def _acts(M, K, seed=0):
+    x = synth.normal_fp16((M, K), seed, 96, M, K)
+    return x, tw.bl_quant_act_int8(dev(x))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 192, 320), (2, 512, 512), (3, 128, 1024),
+                                   (4, 320, 192), (1, 4096, 4096), (1, 1024, 8192),
+                                   (2, 4096, 11008)])
+def test_gemv_acc_and_output(M, N, K):
+    say("gemv", M, N, K)
+    codes, packed = _weights(N, K)
+    x, (q, gamma, rowsum, planes) = _acts(M, K)
+    rq, rg, _ = oracle.quant_act_int8(x)
+    ref_acc = oracle.acc_exact(rq, codes)
+    acc = tw.bl_bitlinear_acc_i32(packed, N, K, planes=planes, path=tw.BL_PATH_GEMV)
+    assert np.array_equal(host(acc), ref_acc)
+    beta = np.float32(synth.BETA_DIRECT)
+    y = tw.bl_bitlinear_gemv(planes, gamma, packed, dev(np.array([beta])), N, K)
+    assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, beta))
+    # per-output-row beta (stacked matrices) and a second run: identical bits
+    betas = synth.uniform_fp16((N,), 0.01, 0.02, 0, 97, N).astype(np.float32)
+    y2 = tw.bl_bitlinear_gemv(planes, gamma, packed, dev(betas), N, K)
+    assert_rel(host(y2), oracle.bitlinear_output(ref_acc, rg, betas))
+    y3 = tw.bl_bitlinear_gemv(planes, gamma, packed, dev(betas), N, K)
+    assert np.array_equal(host(y2).view(np.uint32), host(y3).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (5, 192, 320), (8, 512, 512), (16, 640, 1024),
+                                   (33, 384, 448), (64, 1024, 8192), (100, 256, 640),
+                                   (512, 3200, 3200), (512, 8640, 3200)])
+def test_gemm_acc_and_output(M, N, K):
+    say("gemm", M, N, K)
+    codes, packed = _weights(N, K, seed=1)
+    x, (q, gamma, rowsum, planes) = _acts(M, K, seed=1)
+    rq, rg, _ = oracle.quant_act_int8(x)
+    ref_acc = oracle.acc_exact(rq, codes)
+    acc = tw.bl_bitlinear_acc_i32(packed, N, K, q=q, path=tw.BL_PATH_GEMM)
+    assert np.array_equal(host(acc), ref_acc)
+    beta = np.float32(synth.BETA_DIRECT)
+    y = tw.bl_bitlinear_gemm(q, gamma, packed, dev(np.array([beta])), N)
+    assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, beta))
+    y2 = tw.bl_bitlinear_gemm(q, gamma, packed, dev(np.array([beta])), N)
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_gemv_row_equals_gemm_row():
+    say("gemv vs gemm rows")
+    N, K = 768, 2048
+    codes, packed = _weights(N, K, seed=2)
+    x, (q, gamma, rowsum, planes) = _acts(4, K, seed=2)
+    a1 = host(tw.bl_bitlinear_acc_i32(packed, N, K, planes=planes, path=tw.BL_PATH_GEMV))
+    a2 = host(tw.bl_bitlinear_acc_i32(packed, N, K, q=q, path=tw.BL_PATH_GEMM))
+    assert np.array_equal(a1, a2)
+
+
+@pytest.mark.parametrize("M,N,K,path", [(1, 512, 512, 0), (2, 192, 320, 1), (8, 512, 512, 0),
+                                        (3, 256, 256, 2), (512, 3200, 3200, 0)])
+def test_forward_fp16_in(M, N, K, path):
+    say("forward", M, N, K, path)
+    x = synth.normal_fp16((M, K), 3, 98, M, K)
+    W = synth.normal_fp32((N, K), 3, 99, N, K, std=0.02)
+    packed, beta, _ = tw.bl_ternarize_absmean(dev(W))
+    y = tw.bl_bitlinear_forward(dev(x), packed, beta, N, path=path)
+    codes, rbeta = oracle.ternarize_absmean(W)
+    yref, _, _, _ = oracle.bitlinear_forward(x, codes, rbeta)
+    assert_rel(host(y), yref)
+
+
+def test_config1_tiny_end_to_end():
+    """x fp16 [8, 512] ~ N(0,1), W fp32 [512, 512] ~ N(0, 0.02^2), seed 0, both paths."""
+    say("config1 tiny")
+    x = synth.normal_fp16((8, 512), 0, 1, 0, 10)
+    W = synth.normal_fp32((512, 512), 0, 1, 0, 11, std=0.02)
+    codes, rbeta = oracle.ternarize_absmean(W)
+    yref, acc_ref, rq, _ = oracle.bitlinear_forward(x, codes, rbeta)
+    packed, beta, gcodes = tw.bl_ternarize_absmean(dev(W), want_codes=True)
+    assert np.array_equal(host(gcodes), codes)
+    q, gamma, _, planes = tw.bl_quant_act_int8(dev(x))
+    assert np.array_equal(host(tw.bl_bitlinear_acc_i32(packed, 512, 512, q=q, path=2)), acc_ref)
+    for path in (1, 2):
+        xs = dev(x[:4]) if path == 1 else dev(x)
+        yy = tw.bl_bitlinear_forward(xs, packed, beta, 512, path=path)
+        assert_rel(host(yy), yref[:4] if path == 1 else yref)
+
+
+# ----------------------------------------------------------------------------- OneBit
+def _onebit_inputs(M, N, K, seed=0):
+    x = synth.normal_fp16((M, K), seed, 2, 1, M, K)
+    g = synth.uniform_fp16((K,), 0.5, 1.5, seed, 2, 2, K)
+    h = synth.uniform_fp16((N,), 0.5, 1.5, seed, 2, 3, N)
+    W = synth.normal_fp32((N, K), seed, 2, 4, N, K)
+    return x, g, h, W
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 192, 256), (2, 512, 512), (8, 512, 512),
+                                   (5, 320, 384), (1, 4096, 4096), (16, 4096, 4096)])
+def test_onebit(M, N, K):
+    say("onebit", M, N, K)
+    x, g, h, W = _onebit_inputs(M, N, K)
+    S = np.where(W < 0, -1, 1).astype(np.int8)
+    sp = tw.bl_pack_sign(dev(W))
+    y = tw.bl_onebit_linear(dev(x), dev(g), sp, dev(h))
+    yref = oracle.onebit_forward(x, g, S, h)
+    assert_scaled(host(y), yref, oracle.onebit_error_scale(x, g, h))
+    y2 = tw.bl_onebit_linear(dev(x), dev(g), sp, dev(h))
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- workspace hygiene
+def test_workspace_left_zero():
+    say("workspace zero")
+    N, K = 1024, 8192
+    codes, packed = _weights(N, K, seed=3)
+    x, (q, gamma, rowsum, planes) = _acts(1, K, seed=3)
+    beta = dev(np.array([0.5], np.float32))
+    tw.bl_bitlinear_gemv(planes, gamma, packed, beta, N, K)
+    tw.bl_bitlinear_gemm(q, gamma, packed, beta, N)
+    xo, go, ho, Wo = _onebit_inputs(1, 512, 512)
+    tw.bl_onebit_linear(dev(xo), dev(go), tw.bl_pack_sign(dev(Wo)), dev(ho))
+    torch.cuda.synchronize()
+    zero_prefix = 65536 * 4 + 64 * 65536 * 4        # counters + split-K accumulators
+    for d, buf in tw._ws.items():
+        assert not host(buf[:zero_prefix]).any(), "zero-maintained workspace left dirty"
