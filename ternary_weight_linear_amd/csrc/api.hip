@@ -307,21 +307,19 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
       overlap(y, yb, beta, beta_len * 4) || overlap(y, yb, ws, ws_bytes))
     return BL_ERR_ALIAS;
   char* w = static_cast<char*>(ws);
-  auto* qbuf = reinterpret_cast<int8_t*>(w + L.q_off);
-  auto* pbuf = reinterpret_cast<uint32_t*>(w + L.planes_off);
-  auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
+  auto* wsacc = reinterpret_cast<int32_t*>(w + L.acc_off);
+  auto* wscnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_quant_act(x, M, K, path == BL_PATH_GEMM ? qbuf : nullptr, gbuf, nullptr,
-                                  path == BL_PATH_GEMV ? pbuf : nullptr, s);
-  if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward (quantise)");
-  if (path == BL_PATH_GEMV)
-    e = launch_gemv(pbuf, gbuf, static_cast<int>(M), K, wpacked, beta, beta_len, N, y, nullptr,
-                    reinterpret_cast<int32_t*>(w + L.acc_off),
-                    reinterpret_cast<uint32_t*>(w + L.cnt_off), s);
-  else
-    e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr,
-                    reinterpret_cast<int32_t*>(w + L.acc_off),
-                    reinterpret_cast<uint32_t*>(w + L.cnt_off), s);
+  hipError_t e;
+  if (path == BL_PATH_GEMV) {
+    e = launch_gemv_fused(x, static_cast<int>(M), K, wpacked, beta, beta_len, N, y, wsacc, wscnt, s);
+  } else {
+    auto* qbuf = reinterpret_cast<int8_t*>(w + L.q_off);
+    auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
+    e = launch_quant_act(x, M, K, qbuf, gbuf, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward (quantise)");
+    e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, wscnt, s);
+  }
   return check_launch(e, "bl_bitlinear_forward");
 }
 

@@ -59,6 +59,10 @@ hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                        float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s);
+// Quantise fp16 x inside the GEMV (no separate quantiser launch); M <= 4.
+hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wpacked,
+                             const float* beta, int64_t beta_len, int64_t N, float* y,
+                             int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s);
 hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                        float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
@@ -70,6 +74,40 @@ hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spack
 // ---- device helpers ---------------------------------------------------------------------
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Split-K hand-off between workgroups without cache write-back fences.
+// Partial results move only through agent-scope atomics, which the hardware performs at
+// the device-wide coherence point rather than in one XCD's L2, so no L2 write-back or
+// invalidate is needed (a __threadfence() here costs tens of microseconds per launch).
+// A workgroup waits for its own atomics to complete (s_waitcnt 0) before it increments
+// the tile's completion counter; the workgroup that sees count == nsplit - 1 reads the
+// totals back with atomic exchanges, which also restore the workspace to zero.
+__device__ __forceinline__ void atomic_add_agent(int32_t* p, int32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float atomic_load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t atomic_take_agent(int32_t* p) {
+  return __hip_atomic_exchange(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed, and keep the
+// compiler from moving memory operations across the wait.
+__device__ __forceinline__ void wait_own_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Increment a completion counter; returns the previous count.
+__device__ __forceinline__ uint32_t arrive_agent(uint32_t* cnt) {
+  return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_agent(uint32_t* cnt) {
+  __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace bl

@@ -118,14 +118,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(
         for (int r = 0; r < 4; ++r) {
           const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
           const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
-          if (row < M && col < N) atomicAdd(&ws_acc[row * N + col], acc[i][j][r]);
+          if (row < M && col < N) atomic_add_agent(&ws_acc[row * N + col], acc[i][j][r]);
         }
-    __threadfence();
+    wait_own_memory_ops();
     __syncthreads();
-    if (tid == 0) last_flag = (atomicAdd(&ws_cnt[L], 1u) == gridDim.y - 1);
+    if (tid == 0) last_flag = (arrive_agent(&ws_cnt[L]) == gridDim.y - 1);
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
   }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
         const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
         if (row < M && col < N) {
           int v = acc[i][j][r];
-          if (split) v = atomicExch(&ws_acc[row * N + col], 0);
+          if (split) v = atomic_take_agent(&ws_acc[row * N + col]);
           if (acc_out) acc_out[row * N + col] = v;
           if (y) {
             const float scale = gamma[row] / 127.0f;
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
           }
         }
       }
-  if (split && tid == 0) atomicExch(&ws_cnt[L], 0u);
+  if (split && tid == 0) reset_agent(&ws_cnt[L]);
 }
 
 template <int BM, int BN, int WGM>

@@ -100,16 +100,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   const int64_t n = static_cast<int64_t>(band) * 64 + lane;
   if (nsplit > 1) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) atomicAdd(&ws_acc[m * N + n], acc[m]);
-    __threadfence();
+    for (int m = 0; m < MR; ++m) atomic_add_agent(&ws_acc[m * N + n], acc[m]);
+    wait_own_memory_ops();
     uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(&ws_cnt[band], 1u);
+    if (lane == 0) old = arrive_agent(&ws_cnt[band]);
     old = __shfl(old, 0);
     if (old != static_cast<uint32_t>(nsplit - 1)) return;
-    __threadfence();
 #pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = atomicExch(&ws_acc[m * N + n], 0);
-    if (lane == 0) atomicExch(&ws_cnt[band], 0u);
+    for (int m = 0; m < MR; ++m) acc[m] = atomic_take_agent(&ws_acc[m * N + n]);
+    if (lane == 0) reset_agent(&ws_cnt[band]);
   }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -122,6 +121,160 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   }
 }
 
+// Fused quantise + GEMV: the same add-only product, but each wave builds the activation
+// bit planes of its current tile itself instead of reading X8-64 planes from memory.
+// Every workgroup first reduces |x| over the whole row to gamma (the row is small and
+// stays in L2), then for each tile lane l quantises the input whose plane bit is l and
+// eight wave ballots give the tile's planes directly in scalar registers, where the
+// select + popcount loop wants them. This removes the separate quantiser launch from the
+// decode path; the integer results are identical to bl_quant_act_int8 + GEMV.
+template <int MR>
+__global__ __launch_bounds__(256) void gemv_fused_kernel(
+    const uint16_t* __restrict__ x, int64_t K, const u32x4* __restrict__ W,
+    const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
+    int32_t* __restrict__ ws_acc, uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
+  __shared__ int red[kWaves - 1][MR][64];
+  __shared__ float red_max[kWaves][MR];
+  __shared__ int red_bad[kWaves][MR];
+  const int band = blockIdx.x;
+  const int split = blockIdx.y;
+  const int nsplit = gridDim.y;
+  const int KT = static_cast<int>(K / 64);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = split * tiles_per_split;
+  const int t1 = min(KT, t0 + tiles_per_split);
+  const u32x4* wp = W + static_cast<int64_t>(band) * KT * 64 + lane;
+
+  // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
+  float g[MR];
+  bool zero[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const u32x4* row4 = reinterpret_cast<const u32x4*>(x + m * K);
+    float mx = 0.0f;
+    int bad = 0;
+    for (int64_t i = threadIdx.x; i < K / 8; i += 256) {
+      const u32x4 v = row4[i];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t lo = static_cast<uint16_t>(w4[j] & 0xFFFFu), hi = static_cast<uint16_t>(w4[j] >> 16);
+        bad |= ((lo & 0x7C00u) == 0x7C00u) | ((hi & 0x7C00u) == 0x7C00u);
+        mx = fmaxf(mx, fabsf(half_bits_to_float(lo)));
+        mx = fmaxf(mx, fabsf(half_bits_to_float(hi)));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+      bad |= __shfl_xor(bad, off);
+    }
+    if (lane == 0) { red_max[wave][m] = mx; red_bad[wave][m] = bad; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float mx = red_max[0][m];
+    int bad = red_bad[0][m];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) { mx = fmaxf(mx, red_max[w][m]); bad |= red_bad[w][m]; }
+    g[m] = bad ? __uint_as_float(0x7FC00000u) : mx;
+    zero[m] = bad || mx == 0.0f;
+  }
+
+  // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
+  const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
+
+  int A[MR][8];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) A[m][b] = 0;
+  int cn = 0;
+
+  for (int t = t0 + wave; t < t1; t += kWaves * kUnroll) {
+    u32x4 w[kUnroll];
+    uint16_t xv[kUnroll][MR];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int tt = t + kWaves * u;
+      w[u] = tt < t1 ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < MR; ++m) xv[u][m] = tt < t1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int tt = t + kWaves * u;
+      if (tt < t1) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          int qv = 0;
+          if (!zero[m]) {
+            const float r = rintf(half_bits_to_float(xv[u][m]) * 127.0f / g[m]);
+            qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
+          }
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const unsigned long long mask = __ballot((qv >> b) & 1);
+            const uint32_t x0 = static_cast<uint32_t>(mask), x1 = static_cast<uint32_t>(mask >> 32);
+            A[m][b] += __builtin_popcount((x0 & w[u].x) | (~x0 & w[u].z));
+            A[m][b] += __builtin_popcount((x1 & w[u].y) | (~x1 & w[u].w));
+          }
+        }
+        cn += __builtin_popcount(w[u].z) + __builtin_popcount(w[u].w);
+      }
+    }
+  }
+
+  int acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+    acc[m] = A[m][0] + 2 * A[m][1] + 4 * A[m][2] + 8 * A[m][3] + 16 * A[m][4] + 32 * A[m][5] +
+             64 * A[m][6] - 128 * A[m][7] + cn;
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) red[wave - 1][m][lane] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves - 1; ++w2) acc[m] += red[w2][m][lane];
+
+  const int64_t n = static_cast<int64_t>(band) * 64 + lane;
+  if (nsplit > 1) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) atomic_add_agent(&ws_acc[m * N + n], acc[m]);
+    wait_own_memory_ops();
+    uint32_t old = 0;
+    if (lane == 0) old = arrive_agent(&ws_cnt[band]);
+    old = __shfl(old, 0);
+    if (old != static_cast<uint32_t>(nsplit - 1)) return;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = atomic_take_agent(&ws_acc[m * N + n]);
+    if (lane == 0) reset_agent(&ws_cnt[band]);
+  }
+  const float b = beta[beta_len == 1 ? 0 : n];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) y[m * N + n] = static_cast<float>(acc[m]) * (g[m] / 127.0f) * b;
+}
+
+struct GemvPlan { int64_t nsplit, tps; };
+
+GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
+  const int64_t bands = N / 64;
+  const int64_t KT = K / 64;
+  // Aim for ~1024 workgroups (4 per CU) with at least 8 tiles (2 per wave) each.
+  int64_t nsplit = (1024 + bands / 2) / bands;
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
+  nsplit = std::max<int64_t>(nsplit, 1);
+  if (static_cast<int64_t>(M) * N > kAccCap || bands > kMaxCounters) nsplit = 1;
+  const int64_t tps = (KT + nsplit - 1) / nsplit;
+  return {(KT + tps - 1) / tps, tps};
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_t K,
@@ -129,19 +282,12 @@ hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_
                        float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s) {
   const int64_t bands = N / 64;
-  const int64_t KT = K / 64;
-  // Aim for ~2048 workgroups (8 per CU) with at least 16 tiles (4 per wave) each.
-  int64_t nsplit = (2048 + bands - 1) / bands;
-  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 16));
-  nsplit = std::max<int64_t>(nsplit, 1);
-  if (static_cast<int64_t>(M) * N > kAccCap || bands > kMaxCounters) nsplit = 1;
-  int64_t tps = (KT + nsplit - 1) / nsplit;
-  nsplit = (KT + tps - 1) / tps;
-  const dim3 grid(static_cast<unsigned>(bands), static_cast<unsigned>(nsplit));
+  const GemvPlan p = plan_gemv(M, N, K);
+  const dim3 grid(static_cast<unsigned>(bands), static_cast<unsigned>(p.nsplit));
   const u32x4* W = static_cast<const u32x4*>(wpacked);
 #define BL_GEMV_LAUNCH(MR_)                                                                  \
   hipLaunchKernelGGL(gemv_kernel<MR_>, grid, dim3(256), 0, s, planes, gamma, K, W, beta,     \
-                     beta_len, N, y, acc_out, ws_acc, ws_cnt, static_cast<int>(tps))
+                     beta_len, N, y, acc_out, ws_acc, ws_cnt, static_cast<int>(p.tps))
   switch (M) {
     case 1: BL_GEMV_LAUNCH(1); break;
     case 2: BL_GEMV_LAUNCH(2); break;
@@ -150,6 +296,26 @@ hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_
     default: return hipErrorInvalidValue;
   }
 #undef BL_GEMV_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wpacked,
+                             const float* beta, int64_t beta_len, int64_t N, float* y,
+                             int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
+  const GemvPlan p = plan_gemv(M, N, K);
+  const dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(p.nsplit));
+  const u32x4* W = static_cast<const u32x4*>(wpacked);
+#define BL_GEMVF_LAUNCH(MR_)                                                                 \
+  hipLaunchKernelGGL(gemv_fused_kernel<MR_>, grid, dim3(256), 0, s, x, K, W, beta, beta_len, \
+                     N, y, ws_acc, ws_cnt, static_cast<int>(p.tps))
+  switch (M) {
+    case 1: BL_GEMVF_LAUNCH(1); break;
+    case 2: BL_GEMVF_LAUNCH(2); break;
+    case 3: BL_GEMVF_LAUNCH(3); break;
+    case 4: BL_GEMVF_LAUNCH(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef BL_GEMVF_LAUNCH
   return hipGetLastError();
 }
 

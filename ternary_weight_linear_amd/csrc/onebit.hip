@@ -97,23 +97,21 @@ __global__ __launch_bounds__(256) void onebit_lut_kernel(
     return;
   }
 #pragma unroll
-  for (int m = 0; m < MR; ++m) ws_part[(static_cast<int64_t>(split) * MR + m) * N + n] = acc[m];
-  __threadfence();
+  for (int m = 0; m < MR; ++m) atomic_store_agent(&ws_part[(static_cast<int64_t>(split) * MR + m) * N + n], acc[m]);
+  wait_own_memory_ops();
   uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(&ws_cnt[band], 1u);
+  if (lane == 0) old = arrive_agent(&ws_cnt[band]);
   old = __shfl(old, 0);
   if (old != static_cast<uint32_t>(nsplit - 1)) return;
-  __threadfence();
   const float hn = half_bits_to_float(hvec[n]);
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     float s = 0.0f;
     for (int sp2 = 0; sp2 < nsplit; ++sp2)
-      s += __hip_atomic_load(&ws_part[(static_cast<int64_t>(sp2) * MR + m) * N + n],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s += atomic_load_agent(&ws_part[(static_cast<int64_t>(sp2) * MR + m) * N + n]);
     y[(m0 + m) * N + n] = s * hn;
   }
-  if (lane == 0) atomicExch(&ws_cnt[band], 0u);
+  if (lane == 0) reset_agent(&ws_cnt[band]);
 }
 
 struct OnebitPlan { int mr, tps, nsplit; };

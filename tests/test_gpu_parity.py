@@ -201,7 +201,8 @@ def test_gemv_row_equals_gemm_row():
 
 
 @pytest.mark.parametrize("M,N,K,path", [(1, 512, 512, 0), (2, 192, 320, 1), (8, 512, 512, 0),
-                                        (3, 256, 256, 2), (512, 3200, 3200, 0)])
+                                        (3, 256, 256, 2), (512, 3200, 3200, 0), (3, 256, 640, 1),
+                                        (4, 320, 1024, 1), (1, 10240, 8192, 1), (1, 8192, 28672, 0)])
 def test_forward_fp16_in(M, N, K, path):
     say("forward", M, N, K, path)
     x = synth.normal_fp16((M, K), 3, 98, M, K)
@@ -211,6 +212,24 @@ def test_forward_fp16_in(M, N, K, path):
     codes, rbeta = oracle.ternarize_absmean(W)
     yref, _, _, _ = oracle.bitlinear_forward(x, codes, rbeta)
     assert_rel(host(y), yref)
+
+
+def test_forward_fused_gemv_exact_integers():
+    """Integer-valued x with row max 127 makes q == x; with beta = 1 the fused
+    quantise+GEMV output is acc * 127/127 and must equal the exact accumulators.
+    A row holding NaN must come out NaN."""
+    say("fused gemv integers")
+    N, K = 384, 1024
+    codes, packed = _weights(N, K, seed=4)
+    rg = synth.rng(4, 5)
+    x = rg.integers(-127, 128, size=(3, K)).astype(np.float16)
+    x[:, 0] = 127
+    x[2, 5] = np.float16(np.nan)
+    one = dev(np.array([1.0], np.float32))
+    y = host(tw.bl_bitlinear_forward(dev(x), packed, one, N, path=tw.BL_PATH_GEMV))
+    acc = oracle.acc_exact(x[:2].astype(np.int8), codes)
+    assert np.array_equal(y[:2], acc.astype(np.float32))
+    assert np.all(np.isnan(y[2]))
 
 
 def test_config1_tiny_end_to_end():
