@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--skip-extra", action="store_true", help="only the default workload")
     p.add_argument("--skip-cpu", action="store_true", help="no CPU-oracle baseline")
     p.add_argument("--only", default="", help="run one extra workload by name (profiling)")
+    p.add_argument("--no-graph", action="store_true", help="launch the pass eagerly (profilers)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
@@ -169,7 +170,7 @@ def graphed(torch, fn):
 
 def bench_decode70b(torch, tw, synth, dev, layers, M, steps, warmup, use_graph=True):
     items, full_pass, algo, wbytes, launches = decode_pass(torch, tw, synth, dev, layers, M)
-    ms_eager = timed(torch, full_pass, max(2, steps // 4), 1)
+    ms_eager = timed(torch, full_pass, max(1, steps // 4), 1 if warmup else 0)
     res = dict(ms_per_pass_eager=ms_eager)
     run, keep = (graphed(torch, full_pass) if use_graph else (full_pass, None))
     ms = timed(torch, run, steps, warmup)
@@ -388,15 +389,18 @@ def main():
         res = {}
         if args.only.startswith("decode70b_m"):
             M = int(args.only.split("_m")[1])
-            res = bench_decode70b(torch, tw, synth, dev, layers, M, args.steps, args.warmup)
+            res = bench_decode70b(torch, tw, synth, dev, layers, M, args.steps, args.warmup,
+                                  use_graph=not args.no_graph)
         print(json.dumps({args.only: res}))
         return
 
-    main_res = bench_decode70b(torch, tw, synth, dev, layers, 1, args.steps, args.warmup)
+    main_res = bench_decode70b(torch, tw, synth, dev, layers, 1, args.steps, args.warmup,
+                               use_graph=not args.no_graph)
     log("decode70b M=1:", json.dumps(main_res))
     if not args.skip_extra:
         for M in (8, 32, 64):
-            r = bench_decode70b(torch, tw, synth, dev, layers, M, max(3, args.steps // 4), 1)
+            r = bench_decode70b(torch, tw, synth, dev, layers, M, max(3, args.steps // 4), 1,
+                                use_graph=not args.no_graph)
             extra[f"decode70b_m{M}"] = {k: r[k] for k in ("ms_per_pass", "ms_per_pass_eager", "tokens_per_s", "gbs")}
             log(f"decode70b M={M}:", json.dumps(extra[f'decode70b_m{M}']))
     del layers
