@@ -25,7 +25,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLd = 64 + 16;   // LDS row pitch in bytes (64 k per tile + pad)
 
-template <int BM, int BN, int WGM>
+template <int BM, int BN, int WGM, int S>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ gamma, int64_t M, int64_t K,
     const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
@@ -35,8 +35,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
   static_assert(FM >= 1 && FN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) int8_t As[BM * kLd];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[BN * kLd];
+  constexpr int A_CHUNKS = BM * 4;              // 16-byte chunks of an activation tile
+  constexpr int A_PER = (A_CHUNKS + 255) / 256;
+  constexpr int B_ITEMS = BN * 2;               // (row, half) expansion items
+  constexpr int B_PER = (B_ITEMS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLd];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLd];
   __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
@@ -55,57 +59,88 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   const int t0 = blockIdx.y * tiles_per_split;
   const int t1 = min(KT, t0 + tiles_per_split);
 
+  // Software pipeline: k tiles are fetched from global memory into registers S tiles ahead
+  // of the one being multiplied, staged (weights expanded to int8) into one of two LDS
+  // buffers, then multiplied; one barrier per k tile. The deep register prefetch hides
+  // the global-load latency, which is far longer than one tile's MFMA work.
+  u32x4 ra[S][A_PER];
+  u32x4 rb[S][B_PER];
+  auto fetch = [&](int s, int tk) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + 256 * i;
+      const int64_t row = m0 + (c >> 2);
+      ra[s][i] = u32x4{0, 0, 0, 0};
+      if (c < A_CHUNKS && row < M)
+        ra[s][i] = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + (c & 3) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int c = tid + 256 * i;
+      const int64_t n = n0 + (c >> 1);
+      rb[s][i] = u32x4{0, 0, 0, 0};
+      if (c < B_ITEMS && n < N) rb[s][i] = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
+    }
+  };
+  auto stage = [&](int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + 256 * i;
+      if (c < A_CHUNKS) *reinterpret_cast<u32x4*>(&As[buf][(c >> 2) * kLd + (c & 3) * 16]) = ra[s][i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int c = tid + 256 * i;
+      if (c < B_ITEMS) {
+        const int hh = c & 1;
+        const uint32_t P = hh ? rb[s][i].y : rb[s][i].x, Nm = hh ? rb[s][i].w : rb[s][i].z;
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t pb = (P >> j) & 0x01010101u, nb = (Nm >> j) & 0x01010101u;
+          o[j] = pb + nb * 255u;                // +1 -> 0x01, -1 -> 0xFF per byte
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(&Bs[buf][(c >> 1) * kLd + hh * 32]);
+        dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+        dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+      }
+    }
+  };
+
   i32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  for (int tk = t0; tk < t1; ++tk) {
-    // activations: BM rows x 64 bytes
-    for (int c = tid; c < BM * 4; c += 256) {
-      const int r = c >> 2, part = c & 3;
-      const int64_t row = m0 + r;
-      u32x4 v = {0, 0, 0, 0};
-      if (row < M) v = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + part * 16);
-      *reinterpret_cast<u32x4*>(As + r * kLd + part * 16) = v;
-    }
-    // weights: BN rows x 2 halves of 32 inputs, expanded to int8
-    for (int c = tid; c < BN * 2; c += 256) {
-      const int r = c >> 1, hh = c & 1;
-      const int64_t n = n0 + r;
-      uint32_t o[8];
-      if (n < N) {
-        const u32x4 w = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
-        const uint32_t P = hh ? w.y : w.x, Nm = hh ? w.w : w.z;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pb = (P >> j) & 0x01010101u, nb = (Nm >> j) & 0x01010101u;
-          o[j] = pb + nb * 255u;
-        }
-      } else {
+  for (int s = 0; s < S; ++s)
+    if (t0 + s < t1) fetch(s, t0 + s);
+  for (int kb = t0; kb < t1; kb += S) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = 0;
+    for (int s = 0; s < S; ++s) {
+      const int tk = kb + s;
+      if (tk < t1) {
+        const int buf = (tk - t0) & 1;
+        stage(s, buf);
+        if (tk + S < t1) fetch(s, tk + S);
+        __syncthreads();
+        i32x4 a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          a[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4)]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          b[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4)]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(Bs + r * kLd + hh * 32);
-      dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-      dst[1] = u32x4{o[4], o[5], o[6], o[7]};
     }
-    __syncthreads();
-    i32x4 a[FM], b[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const i32x4*>(As + (wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4));
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      b[j] = *reinterpret_cast<const i32x4*>(Bs + (wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-    __syncthreads();
   }
+  __syncthreads();
 
   // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r (r = 0..3), column l % 16.
   const bool split = gridDim.y > 1;
@@ -147,7 +182,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   if (split && tid == 0) reset_agent(&ws_cnt[L]);
 }
 
-template <int BM, int BN, int WGM>
+// Tuning knobs. Only harnesses that compile this file directly change them; the library
+// itself always runs with these defaults.
+int g_gemm_wg_target = 0;      // workgroups the small-M split-K aims for (0: by M)
+int g_gemm_force = -1;         // tile choice override
+
+template <int BM, int BN, int WGM, int S = 4>
 hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const u32x4* W, const float* beta, int64_t beta_len, int64_t N, float* y,
                        int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
@@ -156,13 +196,15 @@ hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K
   const int64_t tiles = static_cast<int64_t>(MT) * NT;
   int nsplit = 1;
   if (M <= 64) {   // HBM-bound shapes: fill the chip by splitting K (cheap: M x N atomics)
-    nsplit = static_cast<int>(std::min<int64_t>((1024 + tiles - 1) / tiles, std::max(1, KT / 8)));
+    // measured on MI355X: 1024 workgroups suit M <= 16, 512 suit M = 17..64
+    const int64_t target = g_gemm_wg_target ? g_gemm_wg_target : (M <= 16 ? 1024 : 512);
+    nsplit = static_cast<int>(std::min<int64_t>((target + tiles - 1) / tiles, std::max(1, KT / 8)));
     nsplit = std::max(nsplit, 1);
   }
   if (M * N > kAccCap || tiles > kMaxCounters) nsplit = 1;
   const int tps = (KT + nsplit - 1) / nsplit;
   nsplit = (KT + tps - 1) / tps;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM>), dim3(static_cast<unsigned>(tiles), nsplit),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, S>), dim3(static_cast<unsigned>(tiles), nsplit),
                      dim3(256), 0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,
                      ws_cnt, tps, MT, NT);
   return hipGetLastError();
@@ -175,13 +217,39 @@ hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K
                        float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s) {
   const u32x4* W = static_cast<const u32x4*>(wpacked);
-  if (M <= 16)
-    return launch_tile<16, 128, 1>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
-  if (M <= 32)
-    return launch_tile<32, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
-  if (M <= 64)
-    return launch_tile<64, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
-  return launch_tile<128, 128, 2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s);
+#define BL_TILE(BM_, BN_, WGM_) \
+  launch_tile<BM_, BN_, WGM_>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s)
+#define BL_TILES(BM_, BN_, WGM_, S_) \
+  launch_tile<BM_, BN_, WGM_, S_>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s)
+  switch (g_gemm_force) {
+    case 0: return BL_TILE(16, 128, 1);
+    case 1: return BL_TILE(32, 128, 2);
+    case 2: return BL_TILE(64, 128, 2);
+    case 3: return BL_TILE(128, 128, 2);
+    case 4: return BL_TILE(128, 64, 4);
+    case 5: return BL_TILE(64, 64, 2);
+    case 6: return BL_TILE(16, 256, 1);
+    case 7: return BL_TILE(64, 256, 2);
+    case 8: return BL_TILE(128, 256, 2);
+    case 9: return BL_TILE(256, 128, 2);
+    case 10: return BL_TILES(64, 64, 2, 8);
+    case 11: return BL_TILES(128, 128, 2, 8);
+    case 12: return BL_TILES(64, 128, 2, 8);
+    case 13: return BL_TILES(16, 128, 1, 8);
+    case 14: return BL_TILES(32, 128, 2, 8);
+    case 15: return BL_TILES(64, 64, 2, 2);
+    default: break;
+  }
+  if (M <= 16) return BL_TILE(16, 128, 1);
+  if (M <= 32) return BL_TILE(32, 128, 2);
+  if (M <= 64) return BL_TILE(64, 128, 2);
+  // Prefill shapes are small next to 256 CUs (a 512 x 3200 output is 100 tiles of
+  // 128 x 128): 64 x 64 tiles keep every CU busy; wide outputs take 64 x 128.
+  const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
+  if (tiles64 <= 2048) return BL_TILE(64, 64, 2);
+  return BL_TILE(64, 128, 2);
+#undef BL_TILE
+#undef BL_TILES
 }
 
 int64_t gemm_max_tiles(int64_t M, int64_t N) {

@@ -145,6 +145,24 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
   const int t0 = split * tiles_per_split;
   const int t1 = min(KT, t0 + tiles_per_split);
   const u32x4* wp = W + static_cast<int64_t>(band) * KT * 64 + lane;
+  // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
+  const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
+
+  // Software pipeline: weight tiles and the x elements they pair with are loaded one batch
+  // ahead of the batch being reduced. The first batch is issued before gamma is computed,
+  // so the HBM stream starts at once and the row reduction hides under its latency.
+  u32x4 w[kUnroll];
+  uint16_t xv[kUnroll][MR];
+  auto load_batch = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int tt = t + kWaves * u;
+      w[u] = tt < t1 ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < MR; ++m) xv[u][m] = tt < t1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
+    }
+  };
+  load_batch(t0 + wave);
 
   // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
   float g[MR];
@@ -178,13 +196,10 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
     float mx = red_max[0][m];
     int bad = red_bad[0][m];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) { mx = fmaxf(mx, red_max[w][m]); bad |= red_bad[w][m]; }
+    for (int w2 = 1; w2 < kWaves; ++w2) { mx = fmaxf(mx, red_max[w2][m]); bad |= red_bad[w2][m]; }
     g[m] = bad ? __uint_as_float(0x7FC00000u) : mx;
     zero[m] = bad || mx == 0.0f;
   }
-
-  // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
-  const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
 
   int A[MR][8];
 #pragma unroll
@@ -194,15 +209,15 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
   int cn = 0;
 
   for (int t = t0 + wave; t < t1; t += kWaves * kUnroll) {
-    u32x4 w[kUnroll];
-    uint16_t xv[kUnroll][MR];
+    u32x4 wc[kUnroll];
+    uint16_t xc[kUnroll][MR];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int tt = t + kWaves * u;
-      w[u] = tt < t1 ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
+      wc[u] = w[u];
 #pragma unroll
-      for (int m = 0; m < MR; ++m) xv[u][m] = tt < t1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
+      for (int m = 0; m < MR; ++m) xc[u][m] = xv[u][m];
     }
+    if (t + kWaves * kUnroll < t1) load_batch(t + kWaves * kUnroll);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int tt = t + kWaves * u;
@@ -211,18 +226,18 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
         for (int m = 0; m < MR; ++m) {
           int qv = 0;
           if (!zero[m]) {
-            const float r = rintf(half_bits_to_float(xv[u][m]) * 127.0f / g[m]);
+            const float r = rintf(half_bits_to_float(xc[u][m]) * 127.0f / g[m]);
             qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
           }
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             const unsigned long long mask = __ballot((qv >> b) & 1);
             const uint32_t x0 = static_cast<uint32_t>(mask), x1 = static_cast<uint32_t>(mask >> 32);
-            A[m][b] += __builtin_popcount((x0 & w[u].x) | (~x0 & w[u].z));
-            A[m][b] += __builtin_popcount((x1 & w[u].y) | (~x1 & w[u].w));
+            A[m][b] += __builtin_popcount((x0 & wc[u].x) | (~x0 & wc[u].z));
+            A[m][b] += __builtin_popcount((x1 & wc[u].y) | (~x1 & wc[u].w));
           }
         }
-        cn += __builtin_popcount(w[u].z) + __builtin_popcount(w[u].w);
+        cn += __builtin_popcount(wc[u].z) + __builtin_popcount(wc[u].w);
       }
     }
   }
@@ -263,11 +278,17 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
 
 struct GemvPlan { int64_t nsplit, tps; };
 
+// Workgroups the split-K plan aims for (0: by shape). Only tuning harnesses that compile
+// this file directly change it.
+int64_t g_gemv_wg_target = 0;
+
 GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
   const int64_t bands = N / 64;
   const int64_t KT = K / 64;
-  // Aim for ~1024 workgroups (4 per CU) with at least 8 tiles (2 per wave) each.
-  int64_t nsplit = (1024 + bands / 2) / bands;
+  // Split K so the launch has about `target` workgroups (measured on MI355X: ~512 suit
+  // narrow outputs, ~1024 wide ones), keeping at least 8 tiles (2 per wave) per workgroup.
+  const int64_t target = g_gemv_wg_target ? g_gemv_wg_target : (bands < 256 ? 512 : 1024);
+  int64_t nsplit = (target + bands / 2) / bands;
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
   nsplit = std::max<int64_t>(nsplit, 1);
   if (static_cast<int64_t>(M) * N > kAccCap || bands > kMaxCounters) nsplit = 1;
