@@ -380,6 +380,13 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": a.numel()}))
         return
 
+    if args.only in ("prefill3b", "decode7b", "onebit"):
+        fn = {"prefill3b": lambda: bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup),
+              "decode7b": lambda: bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup),
+              "onebit": lambda: bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)}[args.only]
+        print(json.dumps({args.only: fn()}))
+        return
+
     t0 = time.time()
     log("building the 70B-shaped packed stack (17.1 GB) ...")
     layers = build_stack70b(torch, tw, sgpu, synth, dev)
