@@ -49,7 +49,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
     off += b;
   };
   take(static_cast<size_t>(kMaxCounters) * 4, L.cnt_off, L.cnt_bytes);
-  take(static_cast<size_t>(kAccCap) * 4, L.acc_off, L.acc_bytes);
+  take(static_cast<size_t>(kAccCap) * 8, L.acc_off, L.acc_bytes);
   const int64_t mr = std::min<int64_t>(M, 4);
   const int64_t ks = (K % 128 == 0 && N % 64 == 0) ? onebit_splits(M, N, K) : 1;
   take(static_cast<size_t>(ks) * mr * N * 4, L.part_off, L.part_bytes);
@@ -228,7 +228,7 @@ int bl_bitlinear_gemv(const uint32_t* planes, const float* gamma, int64_t M, int
   const WsLayout L = ws_layout(M, N, K);
   char* w = static_cast<char*>(ws);
   return check_launch(launch_gemv(planes, gamma, static_cast<int>(M), K, wpacked, beta, beta_len,
-                                  N, y, nullptr, reinterpret_cast<int32_t*>(w + L.acc_off),
+                                  N, y, nullptr, reinterpret_cast<uint64_t*>(w + L.acc_off),
                                   reinterpret_cast<uint32_t*>(w + L.cnt_off),
                                   static_cast<hipStream_t>(stream)),
                       "bl_bitlinear_gemv");
@@ -250,7 +250,7 @@ int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
   const WsLayout L = ws_layout(M, N, K);
   char* w = static_cast<char*>(ws);
   return check_launch(launch_gemm(q, gamma, M, K, wpacked, beta, beta_len, N, y, nullptr,
-                                  reinterpret_cast<int32_t*>(w + L.acc_off),
+                                  reinterpret_cast<uint64_t*>(w + L.acc_off),
                                   reinterpret_cast<uint32_t*>(w + L.cnt_off),
                                   static_cast<hipStream_t>(stream)),
                       "bl_bitlinear_gemm");
@@ -276,7 +276,7 @@ int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int
       overlap(acc, ab, wpacked, N * K / 4) || overlap(acc, ab, ws, ws_bytes))
     return BL_ERR_ALIAS;
   char* w = static_cast<char*>(ws);
-  auto* wsacc = reinterpret_cast<int32_t*>(w + L.acc_off);
+  auto* wsacc = reinterpret_cast<uint64_t*>(w + L.acc_off);
   auto* wscnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (path == BL_PATH_GEMV)
@@ -307,7 +307,7 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
       overlap(y, yb, beta, beta_len * 4) || overlap(y, yb, ws, ws_bytes))
     return BL_ERR_ALIAS;
   char* w = static_cast<char*>(ws);
-  auto* wsacc = reinterpret_cast<int32_t*>(w + L.acc_off);
+  auto* wsacc = reinterpret_cast<uint64_t*>(w + L.acc_off);
   auto* wscnt = reinterpret_cast<uint32_t*>(w + L.cnt_off);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

@@ -19,10 +19,15 @@ constexpr int kAbsmeanBins = 256;      // one bin per fp32 exponent field value
 // Fixed positions keep one shape's scratch from ever landing on another shape's
 // zero-maintained region when a workspace is shared.
 constexpr int64_t kMaxCounters = 65536;          // completion counters (256 KiB)
-constexpr int64_t kAccCap = int64_t(64) * 65536; // int32 split-K accumulators (16 MiB)
+constexpr int64_t kAccCap = int64_t(64) * 65536; // 64-bit split-K words (32 MiB)
+constexpr int32_t kSplitOffset = int32_t(1) << 23;  // bias that keeps split partials >= 0
+// Integer split-K is used only when every partial fits |p| < kSplitOffset (127 * K below
+// this bound) and at most kMaxIntSplits partials meet in one word.
+constexpr int64_t kMaxIntSplitK = (int64_t(1) << 23) / 127;
+constexpr int kMaxIntSplits = 255;
 struct WsLayout {
   size_t cnt_off, cnt_bytes;       // uint32 completion counters, one per output tile
-  size_t acc_off, acc_bytes;       // int32 [M, N] split-K accumulators
+  size_t acc_off, acc_bytes;       // uint64 [M, N] split-K words (see split_arrive)
   size_t part_off, part_bytes;     // fp32 [KS, M, N] split-K partial sums (OneBit)
   size_t bins_off, bins_bytes;     // uint64 [kAbsmeanBlocks, 256] + flag (absmean)
   size_t q_off, q_bytes;           // int8 [M, K] activations (forward)
@@ -57,15 +62,15 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* q, 
 // y != nullptr: fp32 epilogue into y; acc_out != nullptr: raw int32 accumulators.
 hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s);
 // Quantise fp16 x inside the GEMV (no separate quantiser launch); M <= 4.
 hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wpacked,
                              const float* beta, int64_t beta_len, int64_t N, float* y,
-                             int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s);
+                             uint64_t* ws_acc, uint32_t* ws_cnt, hipStream_t s);
 hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
@@ -95,6 +100,23 @@ __device__ __forceinline__ float atomic_load_agent(const float* p) {
 __device__ __forceinline__ int32_t atomic_take_agent(int32_t* p) {
   return __hip_atomic_exchange(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// One-round-trip split-K reduction of one int32 output element. The workspace word holds
+// (number of arrivals << 32) + sum of (partial + kSplitOffset); each contributor adds its
+// share with one returning atomic at the device coherence point. The contributor whose
+// add brings the count to nsplit is the last one: it alone gets true, reads the exact total
+// from the returned value (no further round trip, no fence) and clears the word.
+__device__ __forceinline__ bool split_arrive(uint64_t* word, int32_t partial, int nsplit,
+                                             int32_t* total) {
+  const uint64_t add = (uint64_t(1) << 32) + static_cast<uint32_t>(partial + kSplitOffset);
+  const uint64_t now =
+      __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+  if ((now >> 32) != static_cast<uint64_t>(nsplit)) return false;
+  *total = static_cast<int32_t>(static_cast<uint32_t>(now) -
+                                static_cast<uint32_t>(nsplit) * static_cast<uint32_t>(kSplitOffset));
+  __hip_atomic_store(word, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // Wait until every memory operation this thread issued has completed, and keep the
 // compiler from moving memory operations across the wait.
 __device__ __forceinline__ void wait_own_memory_ops() {

@@ -29,7 +29,7 @@ template <int BM, int BN, int WGM, int S>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ gamma, int64_t M, int64_t K,
     const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
+    float* __restrict__ y, int32_t* __restrict__ acc_out, uint64_t* __restrict__ ws_acc,
     uint32_t* __restrict__ ws_cnt, int tiles_per_split, int MT, int NT) {
   constexpr int WGN = 4 / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -41,7 +41,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   constexpr int B_PER = (B_ITEMS + 255) / 256;
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLd];
   __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLd];
-  __shared__ uint32_t last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -143,24 +142,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   __syncthreads();
 
   // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r (r = 0..3), column l % 16.
-  const bool split = gridDim.y > 1;
-  if (split) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
-          const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
-          if (row < M && col < N) atomic_add_agent(&ws_acc[row * N + col], acc[i][j][r]);
-        }
-    wait_own_memory_ops();
-    __syncthreads();
-    if (tid == 0) last_flag = (arrive_agent(&ws_cnt[L]) == gridDim.y - 1);
-    __syncthreads();
-    if (!last_flag) return;
-  }
+  const int nsplit = gridDim.y;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -171,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
         const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
         if (row < M && col < N) {
           int v = acc[i][j][r];
-          if (split) v = atomic_take_agent(&ws_acc[row * N + col]);
+          if (nsplit > 1 && !split_arrive(&ws_acc[row * N + col], v, nsplit, &v)) continue;
           if (acc_out) acc_out[row * N + col] = v;
           if (y) {
             const float scale = gamma[row] / 127.0f;
@@ -179,7 +161,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(
           }
         }
       }
-  if (split && tid == 0) reset_agent(&ws_cnt[L]);
 }
 
 // Tuning knobs. Only harnesses that compile this file directly change them; the library
@@ -190,7 +171,7 @@ int g_gemm_force = -1;         // tile choice override
 template <int BM, int BN, int WGM, int S = 4>
 hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const u32x4* W, const float* beta, int64_t beta_len, int64_t N, float* y,
-                       int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
+                       int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
   const int MT = static_cast<int>((M + BM - 1) / BM), NT = static_cast<int>((N + BN - 1) / BN);
   const int KT = static_cast<int>(K / 64);
   const int64_t tiles = static_cast<int64_t>(MT) * NT;
@@ -201,7 +182,8 @@ hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K
     nsplit = static_cast<int>(std::min<int64_t>((target + tiles - 1) / tiles, std::max(1, KT / 8)));
     nsplit = std::max(nsplit, 1);
   }
-  if (M * N > kAccCap || tiles > kMaxCounters) nsplit = 1;
+  if (M * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
+  nsplit = std::min(nsplit, kMaxIntSplits);
   const int tps = (KT + nsplit - 1) / nsplit;
   nsplit = (KT + tps - 1) / tps;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, S>), dim3(static_cast<unsigned>(tiles), nsplit),
@@ -214,7 +196,7 @@ hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K
 
 hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s) {
   const u32x4* W = static_cast<const u32x4*>(wpacked);
 #define BL_TILE(BM_, BN_, WGM_) \

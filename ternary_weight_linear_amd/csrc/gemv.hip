@@ -33,7 +33,7 @@ template <int MR>
 __global__ __launch_bounds__(256) void gemv_kernel(
     const uint32_t* __restrict__ planes, const float* __restrict__ gamma, int64_t K,
     const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
+    float* __restrict__ y, int32_t* __restrict__ acc_out, uint64_t* __restrict__ ws_acc,
     uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
   __shared__ int red[kWaves - 1][MR][64];
   const int band = blockIdx.x;
@@ -98,71 +98,66 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     for (int w = 0; w < kWaves - 1; ++w) acc[m] += red[w][m][lane];
 
   const int64_t n = static_cast<int64_t>(band) * 64 + lane;
-  if (nsplit > 1) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) atomic_add_agent(&ws_acc[m * N + n], acc[m]);
-    wait_own_memory_ops();
-    uint32_t old = 0;
-    if (lane == 0) old = arrive_agent(&ws_cnt[band]);
-    old = __shfl(old, 0);
-    if (old != static_cast<uint32_t>(nsplit - 1)) return;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = atomic_take_agent(&ws_acc[m * N + n]);
-    if (lane == 0) reset_agent(&ws_cnt[band]);
-  }
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    if (acc_out) acc_out[m * N + n] = acc[m];
+    int total = acc[m];
+    if (nsplit > 1 && !split_arrive(&ws_acc[m * N + n], acc[m], nsplit, &total)) continue;
+    if (acc_out) acc_out[m * N + n] = total;
     if (y) {
       const float scale = gamma[m] / 127.0f;
       const float b = beta[beta_len == 1 ? 0 : n];
-      y[m * N + n] = static_cast<float>(acc[m]) * scale * b;
+      y[m * N + n] = static_cast<float>(total) * scale * b;
     }
   }
 }
 
-// Fused quantise + GEMV: the same add-only product, but each wave builds the activation
-// bit planes of its current tile itself instead of reading X8-64 planes from memory.
-// Every workgroup first reduces |x| over the whole row to gamma (the row is small and
-// stays in L2), then for each tile lane l quantises the input whose plane bit is l and
-// eight wave ballots give the tile's planes directly in scalar registers, where the
-// select + popcount loop wants them. This removes the separate quantiser launch from the
-// decode path; the integer results are identical to bl_quant_act_int8 + GEMV.
+// Fused quantise + GEMV: the same add-only product, with the activation bit planes built
+// inside the kernel instead of read from X8-64 memory. A workgroup owns four consecutive
+// 64-row bands (one per wave) and one K range, processed in chunks of up to kChunk tiles:
+//  1. the first weight batch of the wave's band is issued at once, so HBM streaming starts
+//     before anything else;
+//  2. gamma: every workgroup reduces |x| over the whole row. For finite fp16 the magnitude
+//     order equals the integer order of the bits with the sign cleared, so this is an
+//     integer max over masked bit patterns (no conversions); a maximum >= 0x7C00 flags
+//     NaN/inf;
+//  3. each wave quantises every fourth tile of the chunk (lane l takes the input whose plane
+//     bit is l; eight wave ballots give the tile's planes) into LDS, then one barrier;
+//  4. each wave runs the select + popcount loop over the chunk for its own band, weight
+//     loads one batch ahead, planes read from LDS as wave-uniform broadcasts.
+// The integer results are identical to bl_quant_act_int8 followed by the GEMV.
+constexpr int kBatch = 8;
+constexpr int kChunk = 64;                   // tiles whose planes sit in LDS at once
+
 template <int MR>
 __global__ __launch_bounds__(256) void gemv_fused_kernel(
     const uint16_t* __restrict__ x, int64_t K, const u32x4* __restrict__ W,
     const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
-    int32_t* __restrict__ ws_acc, uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
-  __shared__ int red[kWaves - 1][MR][64];
-  __shared__ float red_max[kWaves][MR];
-  __shared__ int red_bad[kWaves][MR];
-  const int band = blockIdx.x;
+    uint64_t* __restrict__ ws_acc, uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
+  __shared__ __attribute__((aligned(16))) uint32_t pl[kChunk][MR][16];
+  __shared__ uint32_t red_max[kWaves][MR];
+  const int64_t nbands = N / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t band = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const bool active = band < nbands;
   const int split = blockIdx.y;
   const int nsplit = gridDim.y;
   const int KT = static_cast<int>(K / 64);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = split * tiles_per_split;
   const int t1 = min(KT, t0 + tiles_per_split);
-  const u32x4* wp = W + static_cast<int64_t>(band) * KT * 64 + lane;
+  const u32x4* wp = W + (active ? band : 0) * KT * 64 + lane;
   // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
   const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
 
-  // Software pipeline: weight tiles and the x elements they pair with are loaded one batch
-  // ahead of the batch being reduced. The first batch is issued before gamma is computed,
-  // so the HBM stream starts at once and the row reduction hides under its latency.
-  u32x4 w[kUnroll];
-  uint16_t xv[kUnroll][MR];
-  auto load_batch = [&](int t) {
+  u32x4 w[kBatch];
+  auto load_batch = [&](int tb, int tend) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tt = t + kWaves * u;
-      w[u] = tt < t1 ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int m = 0; m < MR; ++m) xv[u][m] = tt < t1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
+    for (int u = 0; u < kBatch; ++u) {
+      const int tt = tb + u;
+      w[u] = (active && tt < tend) ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
     }
   };
-  load_batch(t0 + wave);
+  load_batch(t0, min(t1, t0 + kChunk));
 
   // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
   float g[MR];
@@ -170,35 +165,27 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     const u32x4* row4 = reinterpret_cast<const u32x4*>(x + m * K);
-    float mx = 0.0f;
-    int bad = 0;
+    uint32_t mb = 0;
+#pragma unroll 4
     for (int64_t i = threadIdx.x; i < K / 8; i += 256) {
       const u32x4 v = row4[i];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint16_t lo = static_cast<uint16_t>(w4[j] & 0xFFFFu), hi = static_cast<uint16_t>(w4[j] >> 16);
-        bad |= ((lo & 0x7C00u) == 0x7C00u) | ((hi & 0x7C00u) == 0x7C00u);
-        mx = fmaxf(mx, fabsf(half_bits_to_float(lo)));
-        mx = fmaxf(mx, fabsf(half_bits_to_float(hi)));
-      }
+      for (int j = 0; j < 4; ++j) mb = max(mb, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-      bad |= __shfl_xor(bad, off);
-    }
-    if (lane == 0) { red_max[wave][m] = mx; red_bad[wave][m] = bad; }
+    for (int off = 32; off > 0; off >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, off)));
+    if (lane == 0) red_max[wave][m] = mb;
   }
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    float mx = red_max[0][m];
-    int bad = red_bad[0][m];
+    uint32_t mb = red_max[0][m];
 #pragma unroll
-    for (int w2 = 1; w2 < kWaves; ++w2) { mx = fmaxf(mx, red_max[w2][m]); bad |= red_bad[w2][m]; }
-    g[m] = bad ? __uint_as_float(0x7FC00000u) : mx;
-    zero[m] = bad || mx == 0.0f;
+    for (int w2 = 1; w2 < kWaves; ++w2) mb = max(mb, red_max[w2][m]);
+    const bool bad = mb >= 0x7C00u;
+    g[m] = bad ? __uint_as_float(0x7FC00000u) : half_bits_to_float(static_cast<uint16_t>(mb));
+    zero[m] = bad || mb == 0u;
   }
 
   int A[MR][8];
@@ -208,72 +195,105 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
     for (int b = 0; b < 8; ++b) A[m][b] = 0;
   int cn = 0;
 
-  for (int t = t0 + wave; t < t1; t += kWaves * kUnroll) {
-    u32x4 wc[kUnroll];
-    uint16_t xc[kUnroll][MR];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      wc[u] = w[u];
-#pragma unroll
-      for (int m = 0; m < MR; ++m) xc[u][m] = xv[u][m];
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const int c1 = min(t1, c0 + kChunk);
+    if (c0 != t0) {
+      __syncthreads();                    // the previous chunk's planes are consumed
+      load_batch(c0, c1);
     }
-    if (t + kWaves * kUnroll < t1) load_batch(t + kWaves * kUnroll);
+    // quantise tiles c0 + wave + 4j of this chunk into LDS (x loads issued together)
+    constexpr int kPerWave = kChunk / kWaves;
+    uint16_t xq[kPerWave][MR];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tt = t + kWaves * u;
-      if (tt < t1) {
+    for (int j = 0; j < kPerWave; ++j) {
+      const int tt = c0 + wave + kWaves * j;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) xq[j][m] = tt < c1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
+    }
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int tt = c0 + wave + kWaves * j;
+      if (tt < c1) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
           int qv = 0;
           if (!zero[m]) {
-            const float r = rintf(half_bits_to_float(xc[u][m]) * 127.0f / g[m]);
+            const float r = rintf(half_bits_to_float(xq[j][m]) * 127.0f / g[m]);
             qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
           }
+          uint32_t mine = 0;
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             const unsigned long long mask = __ballot((qv >> b) & 1);
-            const uint32_t x0 = static_cast<uint32_t>(mask), x1 = static_cast<uint32_t>(mask >> 32);
-            A[m][b] += __builtin_popcount((x0 & wc[u].x) | (~x0 & wc[u].z));
-            A[m][b] += __builtin_popcount((x1 & wc[u].y) | (~x1 & wc[u].w));
+            if ((lane >> 1) == b) mine = (lane & 1) ? static_cast<uint32_t>(mask >> 32) : static_cast<uint32_t>(mask);
+          }
+          if (lane < 16) pl[tt - c0][m][lane] = mine;
+        }
+      }
+    }
+    __syncthreads();
+    if (active) {
+      for (int tb = c0; tb < c1; tb += kBatch) {
+        u32x4 wc[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) wc[u] = w[u];
+        if (tb + kBatch < c1) load_batch(tb + kBatch, c1);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (tb + u < c1) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+              const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[tb + u - c0][m][0]);
+              const u32x4 p0 = X4[0], p1 = X4[1], p2 = X4[2], p3 = X4[3];
+              const uint32_t X[16] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
+                                      p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
+#pragma unroll
+              for (int b = 0; b < 8; ++b) {
+                const uint32_t x0 = X[2 * b], x1 = X[2 * b + 1];
+                A[m][b] += __builtin_popcount((x0 & wc[u].x) | (~x0 & wc[u].z));
+                A[m][b] += __builtin_popcount((x1 & wc[u].y) | (~x1 & wc[u].w));
+              }
+            }
+            cn += __builtin_popcount(wc[u].z) + __builtin_popcount(wc[u].w);
           }
         }
-        cn += __builtin_popcount(wc[u].z) + __builtin_popcount(wc[u].w);
       }
     }
   }
+  if (!active) return;
 
   int acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m)
     acc[m] = A[m][0] + 2 * A[m][1] + 4 * A[m][2] + 8 * A[m][3] + 16 * A[m][4] + 32 * A[m][5] +
              64 * A[m][6] - 128 * A[m][7] + cn;
-  if (wave > 0) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) red[wave - 1][m][lane] = acc[m];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves - 1; ++w2) acc[m] += red[w2][m][lane];
-
-  const int64_t n = static_cast<int64_t>(band) * 64 + lane;
-  if (nsplit > 1) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) atomic_add_agent(&ws_acc[m * N + n], acc[m]);
-    wait_own_memory_ops();
-    uint32_t old = 0;
-    if (lane == 0) old = arrive_agent(&ws_cnt[band]);
-    old = __shfl(old, 0);
-    if (old != static_cast<uint32_t>(nsplit - 1)) return;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = atomic_take_agent(&ws_acc[m * N + n]);
-    if (lane == 0) reset_agent(&ws_cnt[band]);
-  }
+  const int64_t n = band * 64 + lane;
   const float b = beta[beta_len == 1 ? 0 : n];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) y[m * N + n] = static_cast<float>(acc[m]) * (g[m] / 127.0f) * b;
+  for (int m = 0; m < MR; ++m) {
+    int total = acc[m];
+    if (nsplit > 1 && !split_arrive(&ws_acc[m * N + n], acc[m], nsplit, &total)) continue;
+    y[m * N + n] = static_cast<float>(total) * (g[m] / 127.0f) * b;
+  }
+}
+
+// Split plan of the fused kernel: workgroups own four bands each.
+int64_t g_gemvf_wg_target = 0;   // 0: by shape; changed only by tuning harnesses
+
+struct GemvFusedPlan { int64_t groups, nsplit, tps; };
+
+GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
+  const int64_t bands = N / 64;
+  const int64_t groups = (bands + kWaves - 1) / kWaves;
+  const int64_t KT = K / 64;
+  const int64_t target = g_gemvf_wg_target ? g_gemvf_wg_target : 768;   // measured on MI355X
+  int64_t nsplit = (target + groups / 2) / groups;
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kBatch));
+  nsplit = std::max<int64_t>(nsplit, 1);
+  if (static_cast<int64_t>(M) * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
+  nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
+  const int64_t tps = (KT + nsplit - 1) / nsplit;
+  return {groups, (KT + tps - 1) / tps, tps};
 }
 
 struct GemvPlan { int64_t nsplit, tps; };
@@ -291,7 +311,8 @@ GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
   int64_t nsplit = (target + bands / 2) / bands;
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
   nsplit = std::max<int64_t>(nsplit, 1);
-  if (static_cast<int64_t>(M) * N > kAccCap || bands > kMaxCounters) nsplit = 1;
+  if (static_cast<int64_t>(M) * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
+  nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
   const int64_t tps = (KT + nsplit - 1) / nsplit;
   return {(KT + tps - 1) / tps, tps};
 }
@@ -300,7 +321,7 @@ GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
 
 hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* ws_cnt,
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s) {
   const int64_t bands = N / 64;
   const GemvPlan p = plan_gemv(M, N, K);
@@ -322,9 +343,9 @@ hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_
 
 hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wpacked,
                              const float* beta, int64_t beta_len, int64_t N, float* y,
-                             int32_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
-  const GemvPlan p = plan_gemv(M, N, K);
-  const dim3 grid(static_cast<unsigned>(N / 64), static_cast<unsigned>(p.nsplit));
+                             uint64_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
+  const GemvFusedPlan p = plan_gemv_fused(M, N, K);
+  const dim3 grid(static_cast<unsigned>(p.groups), static_cast<unsigned>(p.nsplit));
   const u32x4* W = static_cast<const u32x4*>(wpacked);
 #define BL_GEMVF_LAUNCH(MR_)                                                                 \
   hipLaunchKernelGGL(gemv_fused_kernel<MR_>, grid, dim3(256), 0, s, x, K, W, beta, beta_len, \
