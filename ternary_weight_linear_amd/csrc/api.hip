@@ -50,9 +50,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
   };
   take(static_cast<size_t>(kMaxCounters) * 4, L.cnt_off, L.cnt_bytes);
   take(static_cast<size_t>(kAccCap) * 8, L.acc_off, L.acc_bytes);
-  const int64_t mr = std::min<int64_t>(M, 4);
-  const int64_t ks = (K % 128 == 0 && N % 64 == 0) ? onebit_splits(M, N, K) : 1;
-  take(static_cast<size_t>(ks) * mr * N * 4, L.part_off, L.part_bytes);
+  take(onebit_part_floats(M, N, K) * 4, L.part_off, L.part_bytes);
   take(static_cast<size_t>(kAbsmeanBlocks) * kAbsmeanBins * 8, L.bins_off, L.bins_bytes);
   take(static_cast<size_t>(M) * K, L.q_off, L.q_bytes);
   take(static_cast<size_t>(M) * K, L.planes_off, L.planes_bytes);

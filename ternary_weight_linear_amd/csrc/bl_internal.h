@@ -37,8 +37,10 @@ struct WsLayout {
 };
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
 
-// Split-K factor of the OneBit kernels for a shape (fixes the workspace size).
+// Split-K factor of the OneBit table kernel, and the fp32 partials either OneBit kernel
+// needs for a shape (fix the workspace size).
 int onebit_splits(int64_t M, int64_t N, int64_t K);
+size_t onebit_part_floats(int64_t M, int64_t N, int64_t K);
 // Number of output tiles (completion counters) the GEMM uses for a shape.
 int64_t gemm_max_tiles(int64_t M, int64_t N);
 

@@ -259,7 +259,8 @@ def _onebit_inputs(M, N, K, seed=0):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 192, 256), (2, 512, 512), (8, 512, 512),
-                                   (5, 320, 384), (1, 4096, 4096), (16, 4096, 4096)])
+                                   (5, 320, 384), (1, 4096, 4096), (16, 4096, 4096), (3, 448, 1024),
+                                   (4, 256, 640), (33, 192, 512), (17, 1024, 8192)])
 def test_onebit(M, N, K):
     say("onebit", M, N, K)
     x, g, h, W = _onebit_inputs(M, N, K)
