@@ -275,6 +275,15 @@ def bench_decode7b(torch, tw, sgpu, synth, dev, steps, warmup, pool=32):
                 gbs=wbytes / (ms / 1e3) / 1e9, us_per_set=ms * 1e3 / pool)
 
 
+def bench_svid(torch, tw, synth, dev, steps, warmup):
+    """SVID initialisation (signs + 20 rounds of power iteration) of a 4096x4096 fp32 weight."""
+    N = K = 4096
+    W = torch.from_numpy(synth.normal_fp32((N, K), 0, 2, 4, 0)).to(dev)
+    ms = timed(torch, lambda: tw.bl_svid_rank1(W, iters=20), max(2, steps // 4), 1)
+    return dict(ms=ms, iters=20, weight_bytes_read_per_iter=2 * N * K * 4,
+                gbs=(2 * 20 + 1) * N * K * 4 / (ms / 1e3) / 1e9)
+
+
 def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
     """OneBit 4096x4096 at M = 1 and 16 over a pool of 256 distinct sign matrices (512 MiB)."""
     N = K = 4096
@@ -419,6 +428,8 @@ def main():
         log("decode7b:", json.dumps(extra["decode7b_m1_pool32"]))
         extra["onebit4096_pool256"] = bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)
         log("onebit:", json.dumps(extra["onebit4096_pool256"]))
+        extra["svid4096"] = bench_svid(torch, tw, synth, dev, args.steps, args.warmup)
+        log("svid:", json.dumps(extra["svid4096"]))
 
     ms = main_res["ms_per_pass"]
     launches = main_res["launches_per_pass"]

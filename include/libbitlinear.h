@@ -178,6 +178,18 @@ int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked,
                      const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* SVID initialisation of a OneBit layer from a float weight ([onebit] "2. 基于 SVID 初始化
+ * 量化模型": sign and magnitude are separated and the magnitude gets a rank-1 approximation,
+ * which the reordered layer uses as its value vectors). Writes S = sign(W) as S1-128 (as
+ * bl_pack_sign) and the rank-1 fit h g^T of |W| found by `iters` rounds of power iteration
+ * (u <- |W| v / ||.||, v <- |W|^T u / ||.||, v_0 = 1/sqrt(K)), with s = || |W|^T u ||:
+ * h = fp16(sqrt(s) u) [N], g = fp16(sqrt(s) v) [K], round to nearest even. sigma (fp32 [1],
+ * may be NULL) receives s. Reductions run in a fixed order (deterministic). W fp32 [N, K],
+ * 16-byte aligned; N % 64 == 0, K % 128 == 0; 1 <= iters <= 1000. Uses ws
+ * (bl_workspace_bytes(1, N, K)). */
+int bl_svid_rank1(const float* W, int64_t N, int64_t K, int iters, void* spacked, uint16_t* g,
+                  uint16_t* h, float* sigma, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

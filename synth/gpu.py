@@ -17,7 +17,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} missing; build with `python -m ternary_weight_linear_amd.build`")
+            raise ImportError(f"{LIB_PATH} missing; build with `python ternary_weight_linear_amd/build.py`")
         _lib = ctypes.CDLL(LIB_PATH)
         _lib.syn_ternary_codes.restype = ctypes.c_int
         _lib.syn_ternary_codes.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,

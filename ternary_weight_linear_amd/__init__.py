@@ -55,6 +55,7 @@ _SIGS = {
     "bl_bitlinear_acc_i32": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
     "bl_bitlinear_forward": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
     "bl_onebit_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "bl_svid_rank1": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -69,9 +70,12 @@ def load_library(path: str = LIB_PATH):
     """dlopen libbitlinear.so and attach the C signatures. Raises if it is not built."""
     if not os.path.exists(path):
         raise ImportError(f"libbitlinear is not built ({path} missing); run "
-                          "`python -m ternary_weight_linear_amd.build` or __graft_entry__.build()")
+                          "`python ternary_weight_linear_amd/build.py` or __graft_entry__.build()")
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
+        if not hasattr(lib, name):
+            raise ImportError(f"{path} lacks {name}: the library is stale; rebuild it with "
+                              "`python ternary_weight_linear_amd/build.py`")
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
@@ -310,6 +314,21 @@ def bl_onebit_linear(x, g, spacked, h, out=None):
     _check(_lib.bl_onebit_linear(_ptr(x), _ptr(g), _ptr(spacked), _ptr(h), M, N, K, _ptr(y),
                                  _ptr(ws), wsb, _stream(d)), "bl_onebit_linear")
     return y
+
+
+def bl_svid_rank1(W, iters: int = 20):
+    """SVID init from fp32 W [N, K]: (S1-128 signs uint8 [N*K/8], g fp16 [K], h fp16 [N], sigma fp32 [1])."""
+    _need(W, torch.float32, "W")
+    d = _dev(W)
+    N, K = W.shape
+    spacked = torch.empty(max(_lib.bl_sign_packed_bytes(N, K), 1), dtype=torch.uint8, device=d)
+    g = torch.empty(K, dtype=torch.float16, device=d)
+    h = torch.empty(N, dtype=torch.float16, device=d)
+    sigma = torch.empty(1, dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, 1, N, K)
+    _check(_lib.bl_svid_rank1(_ptr(W), N, K, iters, _ptr(spacked), _ptr(g), _ptr(h), _ptr(sigma),
+                              _ptr(ws), wsb, _stream(d)), "bl_svid_rank1")
+    return spacked, g, h, sigma
 
 
 __all__ = [n for n in list(globals()) if n.startswith("bl_")] + [

@@ -1,6 +1,9 @@
 """Compile libbitlinear (and the synthetic-input helper library) for gfx950 with hipcc.
 
-    python -m ternary_weight_linear_amd.build        # builds both .so files in-tree
+    python ternary_weight_linear_amd/build.py        # builds both .so files in-tree
+
+Run it as a script (or load it by path): importing the package first would dlopen the
+library that is about to be rebuilt.
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 
-SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "onebit.hip"]
+SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "onebit.hip", "svid.hip"]
 
 
 def _run(cmd):

@@ -55,6 +55,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
   take(static_cast<size_t>(M) * K, L.q_off, L.q_bytes);
   take(static_cast<size_t>(M) * K, L.planes_off, L.planes_bytes);
   take(static_cast<size_t>(M) * 4, L.gamma_off, L.gamma_bytes);
+  take(svid_scratch_floats(N, K) * 4, L.svid_off, L.svid_bytes);
   L.total = off;
   return L;
 }
@@ -319,6 +320,31 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
     e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, wscnt, s);
   }
   return check_launch(e, "bl_bitlinear_forward");
+}
+
+int bl_svid_rank1(const float* W, int64_t N, int64_t K, int iters, void* spacked, uint16_t* g,
+                  uint16_t* h, float* sigma, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !spacked || !g || !h) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
+  if (iters < 1 || iters > 1000) return BL_ERR_ARG;
+  if (!aligned16(W) || !aligned16(spacked)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(1, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t wb = static_cast<size_t>(N) * K * 4;
+  const void* outs[4] = {spacked, g, h, sigma};
+  const size_t outb[4] = {static_cast<size_t>(N) * K / 8, static_cast<size_t>(K) * 2,
+                          static_cast<size_t>(N) * 2, 4};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], W, wb) || overlap(outs[i], outb[i], ws, ws_bytes)) return BL_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return BL_ERR_ALIAS;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_pack_sign(W, N, K, spacked, s);
+  if (e != hipSuccess) return hip_fail(e, "bl_svid_rank1 (signs)");
+  auto* scratch = reinterpret_cast<float*>(static_cast<char*>(ws) + L.svid_off);
+  return check_launch(launch_svid(W, N, K, iters, g, h, sigma, scratch, s), "bl_svid_rank1");
 }
 
 int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked, const uint16_t* h,

@@ -33,6 +33,7 @@ struct WsLayout {
   size_t q_off, q_bytes;           // int8 [M, K] activations (forward)
   size_t planes_off, planes_bytes; // X8-64 planes [M*K bytes] (forward)
   size_t gamma_off, gamma_bytes;   // fp32 [M] (forward)
+  size_t svid_off, svid_bytes;     // fp32 power-iteration vectors (SVID)
   size_t total;
 };
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
@@ -66,6 +67,11 @@ hipError_t launch_gemv(const uint32_t* planes, const float* gamma, int M, int64_
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                        float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s);
+// SVID: rank-1 power iteration on |W| (scratch = svid_scratch_floats(N, K) floats).
+size_t svid_scratch_floats(int64_t N, int64_t K);
+hipError_t launch_svid(const float* W, int64_t N, int64_t K, int iters, uint16_t* g, uint16_t* h,
+                       float* sigma, float* scratch, hipStream_t s);
+
 // Quantise fp16 x inside the GEMV (no separate quantiser launch); M <= 4.
 hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wpacked,
                              const float* beta, int64_t beta_len, int64_t N, float* y,

@@ -4,10 +4,12 @@ and its host-side checks return the documented status before anything is queued.
 The pointers passed here are fake addresses; every call below fails a host check, so no
 HIP call is ever made with them."""
 import ctypes
+import os
 
 import pytest
 
-from ternary_weight_linear_amd.build import LIB_PATH
+LIB_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "ternary_weight_linear_amd", "libbitlinear.so")
 
 OK, NULL, SHAPE, ALIGN, ALIAS, WS, HIP, ARG = range(8)
 
@@ -101,3 +103,8 @@ def test_product_checks(lib):
     assert lib.bl_ternarize_absmean(_p(A), 64, 64, None, None, _p(C), _p(D), 1 << 24, None) == NULL
     assert lib.bl_ternarize_absmean(_p(A), 1 << 17, 1 << 16, None, _p(B), _p(C), _p(D), 1 << 24,
                                     None) == SHAPE
+    svb = lib.bl_workspace_bytes(1, 64, 128)
+    assert lib.bl_svid_rank1(_p(A), 64, 128, 0, _p(B), _p(C), _p(C + 4096), None, _p(D), svb, None) == ARG
+    assert lib.bl_svid_rank1(_p(A), 64, 64, 4, _p(B), _p(C), _p(C + 4096), None, _p(D), svb, None) == SHAPE
+    assert lib.bl_svid_rank1(_p(A), 64, 128, 4, _p(B), _p(C), _p(C + 64), None, _p(D), svb, None) == ALIAS
+    assert lib.bl_svid_rank1(_p(A), 64, 128, 4, _p(B), _p(C), _p(C + 4096), None, _p(D), 64, None) == WS

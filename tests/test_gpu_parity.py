@@ -273,6 +273,55 @@ def test_onebit(M, N, K):
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
 
 
+# ----------------------------------------------------------------------------- SVID
+def _fp16_ulp(a16):
+    a = np.abs(a16.astype(np.float32))
+    return np.spacing(a.astype(np.float16)).astype(np.float32)
+
+
+@pytest.mark.parametrize("N,K,std,kind", [(512, 512, 0.02, "gauss"), (192, 640, 1.0, "gauss"),
+                                          (4096, 4096, 1.0, "gauss"), (256, 384, 1.0, "rank1")])
+def test_svid_rank1(N, K, std, kind):
+    """Power-iteration SVID against the oracle's SVD: signs bit-exact, g and h within one
+    fp16 ulp of the oracle's fp16 values, h g^T within 1e-3 of the fp64 rank-1 fit."""
+    say("svid", N, K, kind)
+    if kind == "rank1":
+        rg = synth.rng(8, 1)
+        W = (np.where(rg.random((N, K)) < 0.5, -1.0, 1.0) *
+             np.outer(rg.uniform(0.5, 2.0, N), rg.uniform(0.5, 2.0, K))).astype(np.float32)
+    else:
+        W = synth.normal_fp32((N, K), 0, 8, N, K, std=std)
+    sp, g, h, sigma = tw.bl_svid_rank1(dev(W), iters=20)
+    S, g16, h16, g64, h64 = oracle.svid_rank1(W.astype(np.float64))
+    assert np.array_equal(host(sp), oracle.pack_sign(W))
+    gg, hh = host(g), host(h)
+    assert np.all(np.abs(gg.astype(np.float32) - g16.astype(np.float32)) <= _fp16_ulp(g16))
+    assert np.all(np.abs(hh.astype(np.float32) - h16.astype(np.float32)) <= _fp16_ulp(h16))
+    ref = np.outer(h64, g64)
+    fit = np.outer(hh.astype(np.float64), gg.astype(np.float64))
+    assert np.linalg.norm(fit - ref) <= 1e-3 * np.linalg.norm(ref)
+    s1 = np.linalg.svd(np.abs(W.astype(np.float64)), compute_uv=False)[0]
+    assert abs(float(host(sigma)[0]) - s1) <= 1e-5 * s1
+
+
+def test_svid_then_onebit_layer():
+    """For a weight whose magnitudes vary by row and column (the structure SVID captures), a
+    layer initialised by SVID on the GPU tracks the float layer better than a
+    per-tensor-scaled sign matrix."""
+    say("svid + onebit")
+    N, K, M = 512, 1024, 4
+    rg = synth.rng(8, 2)
+    W = (synth.normal_fp32((N, K), 0, 8, 99, std=0.02) *
+         np.outer(rg.uniform(0.2, 3.0, N), rg.uniform(0.2, 3.0, K))).astype(np.float32)
+    x = synth.normal_fp16((M, K), 0, 8, 98)
+    sp, g, h, _ = tw.bl_svid_rank1(dev(W))
+    y = host(tw.bl_onebit_linear(dev(x), g, sp, h))
+    yf = x.astype(np.float64) @ W.astype(np.float64).T
+    S = np.where(W < 0, -1.0, 1.0)
+    ys = x.astype(np.float64) @ (np.abs(W).mean() * S).T
+    assert np.linalg.norm(y - yf) < np.linalg.norm(ys - yf)
+
+
 # ----------------------------------------------------------------------------- workspace hygiene
 def test_workspace_left_zero():
     say("workspace zero")
