@@ -120,18 +120,48 @@ def test_billm_storage_golden():
     assert round(n_store, g["printed_decimals"]) == g["n_storing_printed"]
 
 
+def test_pairwise_sum_within_its_error_bound():
+    """The fp32 pairwise tree is within log2(n) * 2^-24 * sum|a| of the exact sum, and
+    equals it when every partial sum is exact (small integers)."""
+    from fractions import Fraction
+    rg = synth.rng(6, 3)
+    a = (rg.standard_normal((40, 128)) * np.exp2(rg.integers(-20, 20, (40, 128)))).astype(np.float32)
+    got = oracle.pairwise_sum_f32(a)
+    for row, s in zip(a, got):
+        exact = sum((Fraction(float(v)) for v in row), Fraction(0))
+        bound = 7 * 2.0 ** -24 * float(sum(abs(float(v)) for v in row))
+        assert abs(float(Fraction(float(s)) - exact)) <= bound
+    ints = rg.integers(-1000, 1000, (5, 128)).astype(np.float32)
+    assert np.array_equal(oracle.pairwise_sum_f32(ints), ints.astype(np.int64).sum(1).astype(np.float32))
+
+
 def test_residual_never_worse_than_direct():
     W = synth.normal_fp32((64, 512), 6, 1)
     Bo, ao, Br, ar = oracle.residual_binarize(W)
-    direct = np.repeat(ao, 128, axis=1) * Bo
-    both = direct + np.repeat(ar, 128, axis=1) * Br
+    direct = np.repeat(ao.astype(np.float64), 128, axis=1) * Bo
+    both = direct + np.repeat(ar.astype(np.float64), 128, axis=1) * Br
     for n in range(64):
         for blk in range(4):
             sl = slice(128 * blk, 128 * blk + 128)
-            assert np.sum((W[n, sl] - both[n, sl]) ** 2) <= np.sum((W[n, sl] - direct[n, sl]) ** 2) + 1e-12
-    Wc = np.where(synth.rng(6, 2).random((64, 256)) < 0.5, -0.3, 0.3)
+            e_both = np.sum((W[n, sl] - both[n, sl]) ** 2)
+            e_dir = np.sum((W[n, sl] - direct[n, sl]) ** 2)
+            assert e_both <= e_dir * (1 + 1e-6)
+    Wc = np.where(synth.rng(6, 2).random((64, 256)) < 0.5, -0.375, 0.375).astype(np.float32)
     Bo, ao, Br, ar = oracle.residual_binarize(Wc)
-    assert np.allclose(ao, 0.3) and np.allclose(ar, 0.0, atol=1e-15)
+    assert np.all(ao == np.float32(0.375)) and np.all(ar == 0)
+    assert np.array_equal(Bo, np.sign(Wc).astype(np.int8))
+
+
+def test_residual_forward_matches_explicit_matrix():
+    W = synth.normal_fp32((64, 256), 6, 4)
+    x = synth.normal_fp16((3, 256), 6, 5)
+    Bo, ao, Br, ar = oracle.residual_binarize(W)
+    y = oracle.residual_forward(x, Bo, ao, Br, ar)
+    Wd = np.zeros((64, 256))
+    for n in range(64):
+        for k in range(256):
+            Wd[n, k] = float(ao[n, k // 128]) * Bo[n, k] + float(ar[n, k // 128]) * Br[n, k]
+    assert np.allclose(y, x.astype(np.float64) @ Wd.T, rtol=0, atol=1e-12)
 
 
 # ----------------------------------------------------------------------------- synthetic inputs
