@@ -297,7 +297,6 @@ def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
             spool.append(torch.roll(spool[s % 4], shifts=s))
     g = torch.from_numpy(synth.uniform_fp16((K,), 0.5, 1.5, 0, 2, 2)).to(dev)
     h = torch.from_numpy(synth.uniform_fp16((N,), 0.5, 1.5, 0, 2, 3)).to(dev)
-    stream = tw._stream(torch.device(dev))
     lib, P = tw._lib, tw.ctypes.c_void_p
     for M in (1, 16):
         x = torch.from_numpy(synth.normal_fp16((M, K), 0, 2, 1)).to(dev)
@@ -306,14 +305,53 @@ def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
         wsp, wsb = P(ws.data_ptr()), ws.numel()
 
         def sweep():
+            stream = P(torch.cuda.current_stream().cuda_stream)   # the capture stream in a graph
             for sp in spool:
                 assert lib.bl_onebit_linear(P(x.data_ptr()), P(g.data_ptr()), P(sp.data_ptr()),
                                             P(h.data_ptr()), M, N, K, P(y.data_ptr()), wsp, wsb, stream) == 0
 
-        ms = timed(torch, sweep, max(2, steps // 4), 1)
-        out[f"M{M}"] = dict(us_per_layer=ms * 1e3 / pool,
+        ms_eager = timed(torch, sweep, max(2, steps // 4), 1)
+        run, keep = graphed(torch, sweep)
+        ms = timed(torch, run, max(2, steps // 4), 1)
+        out[f"M{M}"] = dict(us_per_layer=ms * 1e3 / pool, us_per_layer_eager=ms_eager * 1e3 / pool,
                             gbs_signs=pool * N * K / 8 / (ms / 1e3) / 1e9,
-                            stored_bits_per_layer=8 * spool[0].numel() + 16 * (N + K))
+                            stored_bits_per_layer=8 * spool[0].numel() + 16 * (N + K), graph=True)
+    return out
+
+
+def bench_residual(torch, tw, synth, dev, steps, warmup, pool=128):
+    """Residual-binarised 4096x4096 layers at M = 1 and 16 over a pool of 128 distinct
+    layers (two sign planes + two fp32 scale arrays each: 5 MiB, 640 MiB in all)."""
+    N = K = 4096
+    out = {}
+    layers = []
+    for s in range(pool):
+        if s < 4:
+            W = torch.from_numpy(synth.normal_fp32((N, K), 0, 15, s, std=0.02)).to(dev)
+            layers.append(tw.bl_residual_binarize(W))
+        else:   # distinct layers without host generation: rotate the four binarised ones
+            layers.append(tuple(torch.roll(t, shifts=s) for t in layers[s % 4]))
+    lib, P = tw._lib, tw.ctypes.c_void_p
+    layer_bytes = sum(t.numel() * t.element_size() for t in layers[0])
+    for M in (1, 16):
+        x = torch.from_numpy(synth.normal_fp16((M, K), 0, 15, 100 + M)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = tw.workspace(dev, tw.bl_workspace_bytes(M, N, K))
+        wsp, wsb = P(ws.data_ptr()), ws.numel()
+        ptrs = [[P(t.data_ptr()) for t in L] for L in layers]
+
+        def sweep():
+            stream = P(torch.cuda.current_stream().cuda_stream)   # the capture stream in a graph
+            for po, ao, pr, ar in ptrs:
+                assert lib.bl_residual_linear(P(x.data_ptr()), po, ao, pr, ar, M, N, K,
+                                              P(y.data_ptr()), wsp, wsb, stream) == 0
+
+        ms_eager = timed(torch, sweep, max(2, steps // 4), 1)
+        run, keep = graphed(torch, sweep)
+        ms = timed(torch, run, max(2, steps // 4), 1)
+        out[f"M{M}"] = dict(us_per_layer=ms * 1e3 / pool, us_per_layer_eager=ms_eager * 1e3 / pool,
+                            gbs=pool * layer_bytes / (ms / 1e3) / 1e9, bytes_per_layer=layer_bytes,
+                            graph=True)
     return out
 
 
@@ -389,10 +427,11 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": a.numel()}))
         return
 
-    if args.only in ("prefill3b", "decode7b", "onebit"):
+    if args.only in ("prefill3b", "decode7b", "onebit", "residual"):
         fn = {"prefill3b": lambda: bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup),
               "decode7b": lambda: bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup),
-              "onebit": lambda: bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)}[args.only]
+              "onebit": lambda: bench_onebit(torch, tw, synth, dev, args.steps, args.warmup),
+              "residual": lambda: bench_residual(torch, tw, synth, dev, args.steps, args.warmup)}[args.only]
         print(json.dumps({args.only: fn()}))
         return
 
@@ -427,6 +466,7 @@ def main():
         extra["decode7b_m1_pool32"] = bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup)
         log("decode7b:", json.dumps(extra["decode7b_m1_pool32"]))
         extra["onebit4096_pool256"] = bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)
+        extra["residual4096_pool128"] = bench_residual(torch, tw, synth, dev, args.steps, args.warmup)
         log("onebit:", json.dumps(extra["onebit4096_pool256"]))
         extra["svid4096"] = bench_svid(torch, tw, synth, dev, args.steps, args.warmup)
         log("svid:", json.dumps(extra["svid4096"]))

@@ -13,6 +13,9 @@
  *           two FP16 value vectors g, h; y = ((x ⊙ g) · sign(W)^T) ⊙ h; the 4096x4096 storage
  *           count. "3. 通过知识蒸馏迁移原模型能力": only Sign(W) is kept for inference.
  *           "讨论与分析 / 1. 效率": the element products become bit assignments plus additions.
+ *  [billm]  "BiLLM: Pushing the Limit of Post-Training Quantization for LLMs" blog summary.
+ *           "方法细节", step 2: a weight binarised once plus its residual binarised again;
+ *           "存储位开销分析": two sign bits per weight where the residual is kept.
  *
  * Conventions for every entry point:
  *  - Shapes follow nn.Linear: x is [M, K] row-major (M tokens, K inputs), the weight is
@@ -171,9 +174,9 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
 
 /* OneBit linear ([onebit] "1. 新的1bit结构", Fig. 3): y = ((x ⊙ g) · S^T) ⊙ h with
  * S = sign(W) in S1-128, g fp16 [K] (one per input), h fp16 [N] (one per output),
- * x fp16 [M, K] unquantised, y fp32 [M, N]. t = x*g is exact in fp32; each +-t is t with
- * its sign bit set from the packed bit ("bit assignment"), summed in fp32 in a fixed order.
- * N % 64 == 0, K % 128 == 0. Uses ws. */
+ * x fp16 [M, K] unquantised (16-byte aligned), y fp32 [M, N]. t = x*g is exact in fp32;
+ * each +-t is t with its sign bit set from the packed bit ("bit assignment"), summed in fp32
+ * in a fixed order. N % 64 == 0, K % 128 == 0, M <= 1048560. Uses ws. */
 int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked,
                      const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y, void* ws,
                      size_t ws_bytes, void* stream);
@@ -189,6 +192,31 @@ int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked,
  * (bl_workspace_bytes(1, N, K)). */
 int bl_svid_rank1(const float* W, int64_t N, int64_t K, int iters, void* spacked, uint16_t* g,
                   uint16_t* h, float* sigma, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- residual binarisation ------------------------------------------------------------------ */
+
+/* Residual binarisation of a float weight ([billm] "方法细节", step 2, binary residual
+ * approximation): W ~ alpha_o ⊙ B_o + alpha_r ⊙ B_r. Groups are one output row by 128
+ * consecutive inputs (b = k / 128). For each group:
+ *   alpha_o = fl32(pairwise fp32 sum of |W| over the group's 128 inputs in order) / 128,
+ *   B_o = sign(W) (+1 for +0, -0 and NaN), R = fl32(W - alpha_o B_o),
+ *   alpha_r = fl32(pairwise sum of |R|) / 128, B_r = sign(R).
+ * "Pairwise" is the balanced tree: inputs (0,1), (2,3), ... then pairs of pairs. The sign
+ * planes use S1-128 (bit set iff -1), N*K/8 bytes each; alpha_o and alpha_r are fp32
+ * [N, K/128] row-major (4-byte aligned). A group holding inf/NaN gets non-finite scales.
+ * W fp32 [N, K] (16-byte aligned); N % 64 == 0, K % 128 == 0. Outputs must not overlap W
+ * or each other. */
+int bl_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o, float* alpha_o,
+                         void* planes_r, float* alpha_r, void* stream);
+
+/* Residual-binarised linear: y[m, n] = sum_b alpha_o[n,b] (x_b . B_o[n,b]) +
+ * alpha_r[n,b] (x_b . B_r[n,b]), x_b the 128 inputs of group b. x fp16 [M, K] unquantised
+ * (16-byte aligned), planes and scales from bl_residual_binarize, y fp32 [M, N]. Group dot
+ * products are exact products summed in fp32; the sum over groups runs in a fixed order
+ * for a given shape. N % 64 == 0, K % 128 == 0, M <= 1048560. Uses ws. */
+int bl_residual_linear(const uint16_t* x, const void* planes_o, const float* alpha_o,
+                       const void* planes_r, const float* alpha_r, int64_t M, int64_t N, int64_t K,
+                       float* y, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,5 @@
-"""Python binding of libbitlinear: BitNet b1.58 ternary and OneBit sign-only linear layers
-on MI355X (gfx950).
+"""Python binding of libbitlinear: BitNet b1.58 ternary, OneBit sign-only and
+residual-binarised linear layers on MI355X (gfx950).
 
 Every function here only marshals arguments: it checks tensor dtypes, devices and
 contiguity, allocates outputs with torch (device memory is PyTorch's job) and calls the
@@ -56,6 +56,8 @@ _SIGS = {
     "bl_bitlinear_forward": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, ctypes.c_int, _P, _SZ, _P]),
     "bl_onebit_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "bl_svid_rank1": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
+    "bl_residual_binarize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "bl_residual_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
 }
 
 
@@ -329,6 +331,45 @@ def bl_svid_rank1(W, iters: int = 20):
     _check(_lib.bl_svid_rank1(_ptr(W), N, K, iters, _ptr(spacked), _ptr(g), _ptr(h), _ptr(sigma),
                               _ptr(ws), wsb, _stream(d)), "bl_svid_rank1")
     return spacked, g, h, sigma
+
+
+def bl_residual_binarize(W):
+    """Residual binarisation of fp32 W [N, K]: (planes_o uint8 [N*K/8], alpha_o fp32 [N, K/128],
+    planes_r uint8 [N*K/8], alpha_r fp32 [N, K/128])."""
+    _need(W, torch.float32, "W")
+    d = _dev(W)
+    N, K = W.shape
+    nb = max(_lib.bl_sign_packed_bytes(N, K), 1)
+    po = torch.empty(nb, dtype=torch.uint8, device=d)
+    pr = torch.empty(nb, dtype=torch.uint8, device=d)
+    ao = torch.empty((N, max(K // 128, 1)), dtype=torch.float32, device=d)
+    ar = torch.empty((N, max(K // 128, 1)), dtype=torch.float32, device=d)
+    _check(_lib.bl_residual_binarize(_ptr(W), N, K, _ptr(po), _ptr(ao), _ptr(pr), _ptr(ar),
+                                     _stream(d)), "bl_residual_binarize")
+    return po, ao, pr, ar
+
+
+def bl_residual_linear(x, planes_o, alpha_o, planes_r, alpha_r, out=None):
+    """Residual-binarised layer: fp16 x [M, K] and the outputs of bl_residual_binarize
+    -> y fp32 [M, N]."""
+    _half_bits(x, "x")
+    _need(planes_o, torch.uint8, "planes_o")
+    _need(planes_r, torch.uint8, "planes_r")
+    _need(alpha_o, torch.float32, "alpha_o")
+    _need(alpha_r, torch.float32, "alpha_r")
+    d = _dev(x, planes_o, alpha_o, planes_r, alpha_r)
+    M, K = x.shape
+    N = alpha_o.shape[0]
+    if alpha_o.shape != (N, K // 128) or alpha_r.shape != (N, K // 128):
+        raise ValueError(f"alpha_o/alpha_r must be [N, K/128] = [{N}, {K // 128}]")
+    if planes_o.numel() != N * K // 8 or planes_r.numel() != N * K // 8:
+        raise ValueError(f"planes must hold N*K/8 = {N * K // 8} bytes")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_residual_linear(_ptr(x), _ptr(planes_o), _ptr(alpha_o), _ptr(planes_r),
+                                   _ptr(alpha_r), M, N, K, _ptr(y), _ptr(ws), wsb, _stream(d)),
+           "bl_residual_linear")
+    return y
 
 
 __all__ = [n for n in list(globals()) if n.startswith("bl_")] + [

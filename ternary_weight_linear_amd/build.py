@@ -31,7 +31,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 
-SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "onebit.hip", "svid.hip"]
+SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "onebit.hip", "svid.hip",
+           "residual.hip"]
 
 
 def _run(cmd):

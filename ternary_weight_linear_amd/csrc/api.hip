@@ -33,6 +33,7 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxMtiles = 65535;     // 16-row tiles of x along the grid's y dimension
 
 inline bool dims_ok(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
@@ -50,7 +51,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
   };
   take(static_cast<size_t>(kMaxCounters) * 4, L.cnt_off, L.cnt_bytes);
   take(static_cast<size_t>(kAccCap) * 8, L.acc_off, L.acc_bytes);
-  take(onebit_part_floats(M, N, K) * 4, L.part_off, L.part_bytes);
+  take(std::max(onebit_part_floats(M, N, K), residual_part_floats(M, N, K)) * 4, L.part_off,
+       L.part_bytes);
   take(static_cast<size_t>(kAbsmeanBlocks) * kAbsmeanBins * 8, L.bins_off, L.bins_bytes);
   take(static_cast<size_t>(M) * K, L.q_off, L.q_bytes);
   take(static_cast<size_t>(M) * K, L.planes_off, L.planes_bytes);
@@ -351,8 +353,8 @@ int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked, 
                      int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                      void* stream) {
   if (!x || !g || !spacked || !h || !y) return BL_ERR_NULL;
-  if (!dims_ok(M, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
-  if (!aligned16(spacked)) return BL_ERR_ALIGN;
+  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16) return BL_ERR_SHAPE;
+  if (!aligned16(spacked) || !aligned16(x)) return BL_ERR_ALIGN;
   const WsLayout L = ws_layout(M, N, K);
   if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
@@ -366,6 +368,51 @@ int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked, 
                                     reinterpret_cast<uint32_t*>(w + L.cnt_off),
                                     static_cast<hipStream_t>(stream)),
                       "bl_onebit_linear");
+}
+
+int bl_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o, float* alpha_o,
+                         void* planes_r, float* alpha_r, void* stream) {
+  if (!W || !planes_o || !alpha_o || !planes_r || !alpha_r) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 128 || N * (K / 128) > (int64_t(1) << 32))
+    return BL_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(planes_o) || !aligned16(planes_r)) return BL_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(alpha_o) & 3u) || (reinterpret_cast<uintptr_t>(alpha_r) & 3u))
+    return BL_ERR_ALIGN;
+  const size_t pb = static_cast<size_t>(N) * K / 8, ab = static_cast<size_t>(N) * (K / 128) * 4;
+  const void* outs[4] = {planes_o, alpha_o, planes_r, alpha_r};
+  const size_t outb[4] = {pb, ab, pb, ab};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], W, static_cast<size_t>(N) * K * 4)) return BL_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return BL_ERR_ALIAS;
+  }
+  return check_launch(launch_residual_binarize(W, N, K, planes_o, alpha_o, planes_r, alpha_r,
+                                               static_cast<hipStream_t>(stream)),
+                      "bl_residual_binarize");
+}
+
+int bl_residual_linear(const uint16_t* x, const void* planes_o, const float* alpha_o,
+                       const void* planes_r, const float* alpha_r, int64_t M, int64_t N, int64_t K,
+                       float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !planes_o || !alpha_o || !planes_r || !alpha_r || !y) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16) return BL_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(planes_o) || !aligned16(planes_r)) return BL_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(alpha_o) & 3u) || (reinterpret_cast<uintptr_t>(alpha_r) & 3u))
+    return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4, pb = static_cast<size_t>(N) * K / 8;
+  const size_t ab = static_cast<size_t>(N) * (K / 128) * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, planes_o, pb) || overlap(y, yb, planes_r, pb) ||
+      overlap(y, yb, alpha_o, ab) || overlap(y, yb, alpha_r, ab) || overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  return check_launch(launch_residual_linear(x, planes_o, alpha_o, planes_r, alpha_r, M, N, K, y,
+                                             reinterpret_cast<float*>(w + L.part_off),
+                                             reinterpret_cast<uint32_t*>(w + L.cnt_off),
+                                             static_cast<hipStream_t>(stream)),
+                      "bl_residual_linear");
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ constexpr int kMaxIntSplits = 255;
 struct WsLayout {
   size_t cnt_off, cnt_bytes;       // uint32 completion counters, one per output tile
   size_t acc_off, acc_bytes;       // uint64 [M, N] split-K words (see split_arrive)
-  size_t part_off, part_bytes;     // fp32 [KS, M, N] split-K partial sums (OneBit)
+  size_t part_off, part_bytes;     // fp32 [KS, M, N] split-K partial sums (fp16-input paths)
   size_t bins_off, bins_bytes;     // uint64 [kAbsmeanBlocks, 256] + flag (absmean)
   size_t q_off, q_bytes;           // int8 [M, K] activations (forward)
   size_t planes_off, planes_bytes; // X8-64 planes [M*K bytes] (forward)
@@ -42,6 +42,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
 // needs for a shape (fix the workspace size).
 int onebit_splits(int64_t M, int64_t N, int64_t K);
 size_t onebit_part_floats(int64_t M, int64_t N, int64_t K);
+// fp32 split-K partials of the residual-binarisation forward for a shape.
+size_t residual_part_floats(int64_t M, int64_t N, int64_t K);
 // Number of output tiles (completion counters) the GEMM uses for a shape.
 int64_t gemm_max_tiles(int64_t M, int64_t N);
 
@@ -80,6 +82,14 @@ hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                        float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
                        hipStream_t s);
+// Residual binarisation: two S1-128 sign planes plus fp32 scales [N, K/128] per plane.
+hipError_t launch_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o,
+                                    float* alpha_o, void* planes_r, float* alpha_r,
+                                    hipStream_t s);
+hipError_t launch_residual_linear(const uint16_t* x, const void* planes_o, const float* alpha_o,
+                                  const void* planes_r, const float* alpha_r, int64_t M, int64_t N,
+                                  int64_t K, float* y, float* ws_part, uint32_t* ws_cnt,
+                                  hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);

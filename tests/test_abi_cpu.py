@@ -108,3 +108,37 @@ def test_product_checks(lib):
     assert lib.bl_svid_rank1(_p(A), 64, 64, 4, _p(B), _p(C), _p(C + 4096), None, _p(D), svb, None) == SHAPE
     assert lib.bl_svid_rank1(_p(A), 64, 128, 4, _p(B), _p(C), _p(C + 64), None, _p(D), svb, None) == ALIAS
     assert lib.bl_svid_rank1(_p(A), 64, 128, 4, _p(B), _p(C), _p(C + 4096), None, _p(D), 64, None) == WS
+
+
+def test_residual_checks(lib):
+    N, K = 128, 256
+    KB = K // 128
+    ab = N * KB * 4
+    pb = N * K // 8
+    assert lib.bl_residual_binarize(None, N, K, _p(B), _p(C), _p(B + pb), _p(C + ab), None) == NULL
+    assert lib.bl_residual_binarize(_p(A), N, 192, _p(B), _p(C), _p(B + pb), _p(C + ab), None) == SHAPE
+    assert lib.bl_residual_binarize(_p(A), 96, K, _p(B), _p(C), _p(B + pb), _p(C + ab), None) == SHAPE
+    assert lib.bl_residual_binarize(_p(A), N, K, _p(B + 8), _p(C), _p(B + pb), _p(C + ab), None) == ALIGN
+    assert lib.bl_residual_binarize(_p(A), N, K, _p(B), _p(C + 2), _p(B + pb), _p(C + ab), None) == ALIGN
+    assert lib.bl_residual_binarize(_p(A), N, K, _p(B), _p(C), _p(B + 16), _p(C + ab), None) == ALIAS
+    assert lib.bl_residual_binarize(_p(A), N, K, _p(B), _p(C), _p(B + pb), _p(C + 4), None) == ALIAS
+    assert lib.bl_residual_binarize(_p(A), N, K, _p(A + 64), _p(C), _p(B + pb), _p(C + ab), None) == ALIAS
+    M = 3
+    wsb = lib.bl_workspace_bytes(M, N, K)
+
+    def lin(**kw):
+        a = dict(x=_p(A), po=_p(B), ao=_p(B + pb), pr=_p(B + 2 * pb), ar=_p(B + 2 * pb + ab),
+                 M=M, N=N, K=K, y=_p(C), ws=_p(D), wsb=wsb)
+        a.update(kw)
+        return lib.bl_residual_linear(a["x"], a["po"], a["ao"], a["pr"], a["ar"], a["M"], a["N"],
+                                      a["K"], a["y"], a["ws"], a["wsb"], None)
+    assert lin(ar=None) == NULL
+    assert lin(K=64) == SHAPE
+    assert lin(M=1048561) == SHAPE
+    assert lin(x=_p(A + 2)) == ALIGN
+    assert lin(ao=_p(B + pb + 1)) == ALIGN
+    assert lin(wsb=1024) == WS
+    assert lin(y=_p(B + pb)) == ALIAS
+    assert lin(y=_p(D + 4096)) == ALIAS
+    assert lib.bl_onebit_linear(_p(A + 8), _p(A + 4096), _p(B), _p(B + 8192), 1, 64, 128, _p(C), _p(D),
+                                lib.bl_workspace_bytes(1, 64, 128), None) == ALIGN

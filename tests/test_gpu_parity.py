@@ -1,7 +1,9 @@
 """GPU parity: every libbitlinear entry point against the CPU oracle on the same seeded
 inputs. Integer results (packed bytes, codes, beta bits, int8 activations, bit planes,
-int32 accumulators) must match exactly; fp32 outputs within 1e-3 of the fp64 oracle
-(relative per element for b1.58; against |h| * sum|x g| for OneBit)."""
+int32 accumulators, residual-binarisation signs and scales) must match exactly; fp32
+outputs within 1e-3 of the fp64 oracle (relative per element for b1.58; against
+|h| * sum|x g| for OneBit; against sum_b (|alpha_o| + |alpha_r|) sum_{k in b} |x| for the
+residual format)."""
 import numpy as np
 import pytest
 import torch
@@ -322,6 +324,78 @@ def test_svid_then_onebit_layer():
     assert np.linalg.norm(y - yf) < np.linalg.norm(ys - yf)
 
 
+# ----------------------------------------------------------------------------- residual binarisation
+def _residual_weight(N, K, seed=0):
+    """Gaussian weight with the special groups the format has: an all-zero group, signed
+    zeros, a constant-magnitude group (residual exactly zero), subnormal magnitudes and a
+    group holding inf."""
+    W = synth.normal_fp32((N, K), seed, 12, N, K, std=0.02)
+    W[0, :128] = 0.0
+    W[1, :128] = np.where(synth.rng(seed, 12, 1).random(128) < 0.5, -0.375, 0.375)
+    W[2, :6] = [0.0, -0.0, -0.0, 0.0, -0.0, -0.0]
+    W[3, :128] = synth.normal_fp32(128, seed, 12, 2) * np.float32(1e-39)
+    if N > 64:
+        W[64, :128] = 1.0
+        W[64, 5] = np.inf
+    return W
+
+
+def _bits_equal(a, b):
+    a, b = np.asarray(a, np.float32), np.asarray(b, np.float32)
+    fin = np.isfinite(b)
+    return (np.array_equal(a[fin].view(np.uint32), b[fin].view(np.uint32)) and
+            np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~fin & ~np.isnan(b)],
+                                                                        b[~fin & ~np.isnan(b)]))
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (192, 384), (512, 1024), (4096, 4096)])
+def test_residual_binarize(N, K):
+    """Sign planes bit-exact; both scales bit-exact (same fp32 pairwise order)."""
+    say("residual_binarize", N, K)
+    W = _residual_weight(N, K)
+    po, ao, pr, ar = tw.bl_residual_binarize(dev(W))
+    Bo, ao_ref, Br, ar_ref = oracle.residual_binarize(W)
+    assert np.array_equal(host(po), oracle.pack_sign(Bo.astype(np.float32)))
+    assert np.array_equal(host(pr), oracle.pack_sign(Br.astype(np.float32)))
+    assert _bits_equal(host(ao), ao_ref)
+    assert _bits_equal(host(ar), ar_ref)
+    assert ao_ref[0, 0] == 0 and ar_ref[1, 0] == 0 and 0 < ao_ref[3, 0] < np.float32(1e-38)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 4096, 4096), (2, 320, 384), (3, 192, 1280),
+                                   (5, 448, 1024), (16, 512, 512), (17, 1024, 8192),
+                                   (33, 192, 512), (64, 256, 2048)])
+def test_residual_linear(M, N, K):
+    """Forward on planes and scales packed by the oracle (independent of the GPU packer)."""
+    say("residual_linear", M, N, K)
+    W = synth.normal_fp32((N, K), 0, 13, N, K, std=0.02)
+    x = synth.normal_fp16((M, K), 0, 13, M, K)
+    Bo, ao, Br, ar = oracle.residual_binarize(W)
+    po = dev(oracle.pack_sign(Bo.astype(np.float32)))
+    pr = dev(oracle.pack_sign(Br.astype(np.float32)))
+    y = tw.bl_residual_linear(dev(x), po, dev(ao), pr, dev(ar))
+    yref = oracle.residual_forward(x, Bo, ao, Br, ar)
+    assert_scaled(host(y), yref, oracle.residual_error_scale(x, ao, ar))
+    y2 = tw.bl_residual_linear(dev(x), po, dev(ao), pr, dev(ar))
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_residual_end_to_end_beats_one_plane():
+    """GPU binarise + forward: the two-plane layer tracks the float layer more closely than
+    the first plane alone (the residual's purpose), and matches the oracle."""
+    say("residual end to end")
+    M, N, K = 4, 512, 1024
+    W = synth.normal_fp32((N, K), 0, 14, std=0.02)
+    x = synth.normal_fp16((M, K), 0, 14, 1)
+    po, ao, pr, ar = tw.bl_residual_binarize(dev(W))
+    y = host(tw.bl_residual_linear(dev(x), po, ao, pr, ar))
+    Bo, aor, Br, arr = oracle.residual_binarize(W)
+    assert_scaled(y, oracle.residual_forward(x, Bo, aor, Br, arr), oracle.residual_error_scale(x, aor, arr))
+    yf = x.astype(np.float64) @ W.astype(np.float64).T
+    y1 = oracle.residual_forward(x, Bo, aor, Br, np.zeros_like(arr))
+    assert np.linalg.norm(y - yf) < 0.75 * np.linalg.norm(y1 - yf)
+
+
 # ----------------------------------------------------------------------------- workspace hygiene
 def test_workspace_left_zero():
     say("workspace zero")
@@ -333,6 +407,7 @@ def test_workspace_left_zero():
     tw.bl_bitlinear_gemm(q, gamma, packed, beta, N)
     xo, go, ho, Wo = _onebit_inputs(1, 512, 512)
     tw.bl_onebit_linear(dev(xo), dev(go), tw.bl_pack_sign(dev(Wo)), dev(ho))
+    tw.bl_residual_linear(dev(xo), *tw.bl_residual_binarize(dev(Wo)))
     torch.cuda.synchronize()
     zero_prefix = 65536 * 4 + 64 * 65536 * 8        # counters + split-K words
     for d, buf in tw._ws.items():
