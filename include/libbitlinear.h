@@ -47,9 +47,12 @@
  *    (m*(K/64) + t)*16; word 2b + h holds bit b (two's complement, b = 0..7) of
  *    q[m, 64t + 32h + c] at the same bit positions as T2-PN-64. M*K bytes.
  *  S1-128 (sign). N % 64 == 0, K % 128 == 0. Tile (tn, tk) = rows 64tn..+63, inputs
- *    128tk..+127, 1024 bytes at byte (tn*(K/128) + tk)*1024. Row r = bytes 16r..16r+15 =
- *    uint32 W_0..W_3; W_h covers k = 128tk + 32h + c; c = 2p is bit p and c = 2p+1 is
- *    bit 16+p (p = 0..15). Bit set iff the weight is -1. N*K/8 bytes.
+ *    128tk..+127, 1024 bytes at byte (tn*(K/128) + tk)*1024, read as 256 uint32 words.
+ *    Tile row r = 16f + u (f = 0..3, u = 0..15) and tile input c = 32s + 8g + 2q + e
+ *    (s, g, q = 0..3; e = 0..1) sit in word 4*(16g + u) + f at bit 16e + 4s + q. Bit set
+ *    iff the weight is -1. N*K/8 bytes. (Lane 16g + u of a wave loads the 16 bytes at
+ *    16*(16g + u): exactly the signs its fp16 matrix-core operands need, and one shift
+ *    puts each pair of them at bits 15 and 31.)
  */
 #ifndef LIBBITLINEAR_H
 #define LIBBITLINEAR_H
@@ -176,7 +179,7 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
  * S = sign(W) in S1-128, g fp16 [K] (one per input), h fp16 [N] (one per output),
  * x fp16 [M, K] unquantised (16-byte aligned), y fp32 [M, N]. t = x*g is exact in fp32;
  * each +-t is t with its sign bit set from the packed bit ("bit assignment"), summed in fp32
- * in a fixed order. N % 64 == 0, K % 128 == 0, M <= 1048560. Uses ws. */
+ * in a fixed order. N % 64 == 0, K % 128 == 0, K <= 2^26, M <= 1048560. Uses ws. */
 int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked,
                      const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y, void* ws,
                      size_t ws_bytes, void* stream);
@@ -213,7 +216,7 @@ int bl_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o, f
  * alpha_r[n,b] (x_b . B_r[n,b]), x_b the 128 inputs of group b. x fp16 [M, K] unquantised
  * (16-byte aligned), planes and scales from bl_residual_binarize, y fp32 [M, N]. Group dot
  * products are exact products summed in fp32; the sum over groups runs in a fixed order
- * for a given shape. N % 64 == 0, K % 128 == 0, M <= 1048560. Uses ws. */
+ * for a given shape. N % 64 == 0, K % 128 == 0, K <= 2^26, M <= 1048560. Uses ws. */
 int bl_residual_linear(const uint16_t* x, const void* planes_o, const float* alpha_o,
                        const void* planes_r, const float* alpha_r, int64_t M, int64_t N, int64_t K,
                        float* y, void* ws, size_t ws_bytes, void* stream);

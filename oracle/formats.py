@@ -22,9 +22,10 @@ X8-64 (activation bit planes of int8 q, used by the add-only GEMV).
 
 S1-128 (sign, 1 bit/weight). N % 64 == 0, K % 128 == 0.
   Tile (tn, tk) = rows 64tn.., inputs 128tk.., 1024 bytes at byte
-  (tn*(K/128) + tk)*1024. Row r = bytes 16r..16r+15 = four little-endian uint32
-  words W_0..W_3. Word W_h covers k = 128tk + 32h + c; c = 2p sits at bit p and
-  c = 2p + 1 at bit 16 + p (p = 0..15). Bit set iff the weight is -1.
+  (tn*(K/128) + tk)*1024, read as 256 little-endian uint32 words. Tile row
+  r = 16f + u (f, u: 0..3, 0..15) and tile input c = 32s + 8g + 2q + e
+  (s, g, q: 0..3; e: 0..1) sit in word 4*(16g + u) + f at bit 16e + 4s + q.
+  Bit set iff the weight is -1.
 """
 from __future__ import annotations
 
@@ -93,11 +94,12 @@ def _s1_byte_and_bit(N: int, K: int):
     n = np.arange(N, dtype=np.int64)[:, None]
     k = np.arange(K, dtype=np.int64)[None, :]
     tn, r = n // 64, n % 64
-    tk, kk = k // 128, k % 128
-    h, c = kk // 32, kk % 32
-    wbit = np.where(c % 2 == 0, c // 2, 16 + c // 2)   # c = 2p -> bit p, c = 2p+1 -> bit 16+p
-    word = (tn * (K // 128) + tk) * 1024 + 16 * r + 4 * h
-    byte = word + wbit // 8
+    tk, c = k // 128, k % 128
+    f, u = r // 16, r % 16
+    s, g, q, e = c // 32, (c // 8) % 4, (c // 2) % 4, c % 2
+    word = 4 * (16 * g + u) + f
+    wbit = 16 * e + 4 * s + q
+    byte = (tn * (K // 128) + tk) * 1024 + 4 * word + wbit // 8
     return byte, np.broadcast_to(wbit % 8, byte.shape)
 
 

@@ -34,6 +34,7 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxMtiles = 65535;     // 16-row tiles of x along the grid's y dimension
+constexpr int64_t kMaxSignK = int64_t(1) << 26;   // fp16-input kernels use 32-bit row offsets
 
 inline bool dims_ok(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
@@ -353,7 +354,8 @@ int bl_onebit_linear(const uint16_t* x, const uint16_t* g, const void* spacked, 
                      int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                      void* stream) {
   if (!x || !g || !spacked || !h || !y) return BL_ERR_NULL;
-  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16) return BL_ERR_SHAPE;
+  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16 || K > kMaxSignK)
+    return BL_ERR_SHAPE;
   if (!aligned16(spacked) || !aligned16(x)) return BL_ERR_ALIGN;
   const WsLayout L = ws_layout(M, N, K);
   if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
@@ -395,7 +397,8 @@ int bl_residual_linear(const uint16_t* x, const void* planes_o, const float* alp
                        const void* planes_r, const float* alpha_r, int64_t M, int64_t N, int64_t K,
                        float* y, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !planes_o || !alpha_o || !planes_r || !alpha_r || !y) return BL_ERR_NULL;
-  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16) return BL_ERR_SHAPE;
+  if (!dims_ok(M, N, K) || N % 64 || K % 128 || M > kMaxMtiles * 16 || K > kMaxSignK)
+    return BL_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(planes_o) || !aligned16(planes_r)) return BL_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(alpha_o) & 3u) || (reinterpret_cast<uintptr_t>(alpha_r) & 3u))
     return BL_ERR_ALIGN;

@@ -38,9 +38,7 @@ struct WsLayout {
 };
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
 
-// Split-K factor of the OneBit table kernel, and the fp32 partials either OneBit kernel
-// needs for a shape (fix the workspace size).
-int onebit_splits(int64_t M, int64_t N, int64_t K);
+// fp32 split-K partials of the OneBit forward for a shape (fix the workspace size).
 size_t onebit_part_floats(int64_t M, int64_t N, int64_t K);
 // fp32 split-K partials of the residual-binarisation forward for a shape.
 size_t residual_part_floats(int64_t M, int64_t N, int64_t K);

@@ -14,8 +14,6 @@ namespace {
 
 // Bit position of input c (0..31) inside a T2-PN-64 / X8-64 word: c = 4j + i -> 8i + j.
 __device__ __forceinline__ int t2_bit(int c) { return 8 * (c & 3) + (c >> 2); }
-// Bit position of input c (0..31) inside an S1-128 word: c = 2p -> p, c = 2p+1 -> 16 + p.
-__device__ __forceinline__ int s1_bit(int c) { return (c & 1) * 16 + (c >> 1); }
 
 __global__ void fill_zero_kernel(uint4* p16, size_t n16, unsigned char* tail, size_t ntail) {
   size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -85,51 +83,57 @@ __global__ void unpack_ternary_kernel(const uint4* __restrict__ in, int64_t N, i
   if (bad && n_invalid) atomicAdd(n_invalid, bad);
 }
 
-// float W [N, K] -> S1-128. Thread g <-> (tile of 64 x 128 = g / 64, row r = g % 64).
+// float W [N, K] -> S1-128. Thread i <-> one 16-byte record: tile i / 64, record L = i % 64
+// = 16g + u, holding word f (rows 16f + u) with the signs of tile inputs 32s + 8g + j,
+// j = 2q + e, at bit 16e + 4s + q.
 __global__ void pack_sign_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                  uint4* __restrict__ out) {
   const int64_t KT = K / 128;
-  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (g >= N * KT) return;
-  const int64_t tile = g >> 6, r = g & 63;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= N * KT) return;
+  const int64_t tile = i >> 6;
+  const int L = static_cast<int>(i & 63), g = L >> 4, u = L & 15;
   const int64_t tn = tile / KT, tk = tile % KT;
-  const int64_t n = tn * 64 + r;
-  const float4* src = reinterpret_cast<const float4*>(W + n * K + tk * 128);
   uint32_t S[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int v4 = 0; v4 < 32; ++v4) {
-    const float4 v = src[v4];
-    const float e[4] = {v.x, v.y, v.z, v.w};
+  for (int f = 0; f < 4; ++f) {
+    const float* row = W + (tn * 64 + 16 * f + u) * K + tk * 128 + 8 * g;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = v4 * 4 + u;            // 0..127
-      if (e[u] < 0.0f) S[kk >> 5] |= 1u << s1_bit(kk & 31);
+    for (int s = 0; s < 4; ++s) {
+      const float4 lo = reinterpret_cast<const float4*>(row + 32 * s)[0];
+      const float4 hi = reinterpret_cast<const float4*>(row + 32 * s)[1];
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (v[j] < 0.0f) S[f] |= 1u << (16 * (j & 1) + 4 * s + (j >> 1));
     }
   }
-  out[g] = make_uint4(S[0], S[1], S[2], S[3]);
+  out[i] = make_uint4(S[0], S[1], S[2], S[3]);
 }
 
 __global__ void unpack_sign_kernel(const uint4* __restrict__ in, int64_t N, int64_t K,
                                    int8_t* __restrict__ signs) {
   const int64_t KT = K / 128;
-  const int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (g >= N * KT) return;
-  const int64_t tile = g >> 6, r = g & 63;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= N * KT) return;
+  const int64_t tile = i >> 6;
+  const int L = static_cast<int>(i & 63), g = L >> 4, u = L & 15;
   const int64_t tn = tile / KT, tk = tile % KT;
-  const int64_t n = tn * 64 + r;
-  const uint4 w = in[g];
+  const uint4 w = in[i];
   const uint32_t S[4] = {w.x, w.y, w.z, w.w};
-  uint4* dst = reinterpret_cast<uint4*>(signs + n * K + tk * 128);
 #pragma unroll
-  for (int chunk = 0; chunk < 8; ++chunk) {
-    uint32_t o[4] = {0, 0, 0, 0};
+  for (int f = 0; f < 4; ++f) {
+    int8_t* row = signs + (tn * 64 + 16 * f + u) * K + tk * 128 + 8 * g;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const int kk = chunk * 16 + b;
-      const uint32_t neg = (S[kk >> 5] >> s1_bit(kk & 31)) & 1u;
-      o[b >> 2] |= (neg ? 0xFFu : 0x01u) << (8 * (b & 3));
+    for (int s = 0; s < 4; ++s) {
+      uint32_t o[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t neg = (S[f] >> (16 * (j & 1) + 4 * s + (j >> 1))) & 1u;
+        o[j >> 2] |= (neg ? 0xFFu : 0x01u) << (8 * (j & 3));
+      }
+      reinterpret_cast<uint2*>(row + 32 * s)[0] = make_uint2(o[0], o[1]);
     }
-    dst[chunk] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 

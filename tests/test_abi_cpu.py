@@ -135,6 +135,7 @@ def test_residual_checks(lib):
     assert lin(ar=None) == NULL
     assert lin(K=64) == SHAPE
     assert lin(M=1048561) == SHAPE
+    assert lin(K=(1 << 26) + 128) == SHAPE
     assert lin(x=_p(A + 2)) == ALIGN
     assert lin(ao=_p(B + pb + 1)) == ALIGN
     assert lin(wsb=1024) == WS

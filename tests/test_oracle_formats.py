@@ -71,20 +71,33 @@ def test_t2_invalid_codes():
 
 # ----------------------------------------------------------------------------- S1-128
 @pytest.mark.parametrize("n,k,byte,value", [
-    (0, 0, 0, 0x01),       # c = 0 -> bit 0
-    (0, 1, 2, 0x01),       # c = 1 = 2*0+1 -> bit 16 -> byte 2 bit 0
-    (0, 2, 0, 0x02),       # c = 2 -> p = 1 -> bit 1
-    (0, 33, 6, 0x01),      # word 1 (bytes 4..7), c = 1 -> bit 16 -> byte 6
-    (1, 31, 19, 0x80),     # row 1 at 16; c = 31 -> bit 31 -> byte 19 bit 7
-    (0, 128, 1024, 0x01),  # tile (0, 1)
+    (0, 0, 0, 0x01),        # r = 0, c = 0 -> word 0, bit 0
+    (0, 1, 2, 0x01),        # e = 1 -> bit 16 -> byte 2 bit 0
+    (0, 2, 0, 0x02),        # q = 1 -> bit 1
+    (0, 32, 0, 0x10),       # s = 1 -> bit 4
+    (0, 8, 256, 0x01),      # g = 1 -> word 64 -> byte 256
+    (1, 0, 16, 0x01),       # u = 1 -> word 4 -> byte 16
+    (16, 0, 4, 0x01),       # f = 1 -> word 1 -> byte 4
+    (0, 127, 771, 0x80),    # c = 96 + 24 + 6 + 1 -> word 192, bit 31 -> byte 771 bit 7
+    (63, 127, 1023, 0x80),  # f = 3, u = 15 -> word 255, bit 31
+    (0, 128, 1024, 0x01),   # tile (0, 1)
+    (64, 0, 2048, 0x01),    # tile (1, 0) of a 128 x 256 matrix
 ])
 def test_s1_worked_bytes(n, k, byte, value):
-    W = np.ones((64, 256), dtype=np.float32)
+    W = np.ones((128, 256), dtype=np.float32)
     W[n, k] = -0.25
     packed = oracle.pack_sign(W)
     expect = np.zeros_like(packed)
     expect[byte] = value
     assert np.array_equal(packed, expect)
+
+
+def test_s1_layout_is_a_bijection():
+    """Every (row, input) of a tile gets its own bit: the 64 x 128 one-hot matrices pack to
+    64 * 128 distinct single-bit patterns covering all 8192 bits of the tile."""
+    byte, bit = oracle.formats._s1_byte_and_bit(64, 128)
+    pos = (byte * 8 + bit).ravel()
+    assert np.array_equal(np.sort(pos), np.arange(8192))
 
 
 def test_s1_round_trip_and_zero_reading():
