@@ -112,33 +112,49 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 }
 
 // Fused quantise + GEMV: the same add-only product, with the activation bit planes built
-// inside the kernel instead of read from X8-64 memory. A workgroup owns four consecutive
+// inside the kernel instead of read from X8-64 memory. A workgroup owns kFW consecutive
 // 64-row bands (one per wave) and one K range, processed in chunks of up to kChunk tiles:
-//  1. the first weight batch of the wave's band is issued at once, so HBM streaming starts
-//     before anything else;
+//  1. loads are issued at once: first this thread's share of the row for gamma and the x
+//     values its wave quantises in the first chunk, then the wave's first kRing - 1 weight
+//     batches, so HBM streaming starts before anything else (vector loads complete in
+//     issue order, so the x-dependent steps never wait for weights);
 //  2. gamma: every workgroup reduces |x| over the whole row. For finite fp16 the magnitude
 //     order equals the integer order of the bits with the sign cleared, so this is an
 //     integer max over masked bit patterns (no conversions); a maximum >= 0x7C00 flags
 //     NaN/inf;
-//  3. each wave quantises every fourth tile of the chunk (lane l takes the input whose plane
+//  3. each wave quantises every kFW-th tile of the chunk (lane l takes the input whose plane
 //     bit is l; eight wave ballots give the tile's planes) into LDS, then one barrier;
-//  4. each wave runs the select + popcount loop over the chunk for its own band, weight
-//     loads one batch ahead, planes read from LDS as wave-uniform broadcasts.
+//  4. each wave runs the select + popcount loop over the chunk for its own band with a ring
+//     of kRing register batches, kRing - 1 of them in flight, planes read from LDS as
+//     wave-uniform broadcasts.
 // The integer results are identical to bl_quant_act_int8 followed by the GEMV.
-constexpr int kBatch = 8;
-constexpr int kChunk = 64;                   // tiles whose planes sit in LDS at once
+#ifndef BL_GEMVF_BATCH
+#define BL_GEMVF_BATCH 8
+#endif
+#ifndef BL_GEMVF_RING
+#define BL_GEMVF_RING 2
+#endif
+constexpr int kBatch = BL_GEMVF_BATCH;      // tiles per register batch
+constexpr int kRing = BL_GEMVF_RING;        // register batches per wave
+constexpr int kChunk = 64;                  // tiles whose planes sit in LDS at once
+#ifndef BL_GEMVF_WAVES
+#define BL_GEMVF_WAVES 4
+#endif
+constexpr int kFW = BL_GEMVF_WAVES;         // waves (bands) per workgroup
 
-template <int MR>
-__global__ __launch_bounds__(256) void gemv_fused_kernel(
+constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chunk
+
+template <int MR, int GL>
+__global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
     const uint16_t* __restrict__ x, int64_t K, const u32x4* __restrict__ W,
     const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
     uint64_t* __restrict__ ws_acc, uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
   __shared__ __attribute__((aligned(16))) uint32_t pl[kChunk][MR][16];
-  __shared__ uint32_t red_max[kWaves][MR];
+  __shared__ uint32_t red_max[kFW][MR];
   const int64_t nbands = N / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t band = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t band = static_cast<int64_t>(blockIdx.x) * kFW + wave;
   const bool active = band < nbands;
   const int split = blockIdx.y;
   const int nsplit = gridDim.y;
@@ -149,29 +165,60 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
   // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
   const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
 
-  u32x4 w[kBatch];
-  auto load_batch = [&](int tb, int tend) {
+  // All loads below are unconditional (indices past the range are clamped to its last
+  // tile, and such values are never used): branch-free code lets the compiler wait for
+  // exactly the loads a step needs instead of for every load in flight.
+  u32x4 w[kRing][kBatch];
+  auto load_batch = [&](u32x4 (&dst)[kBatch], int tb, int tend) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int tt = tb + u;
-      w[u] = (active && tt < tend) ? wp[static_cast<int64_t>(tt) * 64] : u32x4{0, 0, 0, 0};
+    for (int u = 0; u < kBatch; ++u) dst[u] = wp[static_cast<int64_t>(min(tb + u, tend - 1)) * 64];
+  };
+  auto load_x = [&](uint16_t (&xq)[kPerWave][MR], int c0, int c1) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int tt = min(c0 + wave + kFW * j, c1 - 1);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) xq[j][m] = x[m * K + 64 * tt + koff];
     }
   };
-  load_batch(t0, min(t1, t0 + kChunk));
+  // Vector loads complete in issue order, so everything that waits only on x is issued
+  // before the weights: this thread's share of the row for gamma (GL loads per row when
+  // GL > 0, i.e. K <= 2048 GL) and the x values it quantises in the first chunk.
+  const u32x4* const row4 = reinterpret_cast<const u32x4*>(x);
+  const int64_t K8 = K / 8;
+  u32x4 gx[MR][GL > 0 ? GL : 1];
+  if constexpr (GL > 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < GL; ++i)   // repeated elements do not change the maximum
+        gx[m][i] = row4[m * K8 + min<int64_t>(threadIdx.x + 64 * kFW * i, K8 - 1)];
+  }
+  uint16_t xq[kPerWave][MR];
+  load_x(xq, t0, min(t1, t0 + kChunk));
+  {
+    const int c1 = min(t1, t0 + kChunk);
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r) load_batch(w[r], t0 + r * kBatch, c1);
+  }
 
   // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
   float g[MR];
   bool zero[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    const u32x4* row4 = reinterpret_cast<const u32x4*>(x + m * K);
     uint32_t mb = 0;
-#pragma unroll 4
-    for (int64_t i = threadIdx.x; i < K / 8; i += 256) {
-      const u32x4 v = row4[i];
+    auto fold = [&](const u32x4& v) {
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) mb = max(mb, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
+    };
+    if constexpr (GL > 0) {
+#pragma unroll
+      for (int i = 0; i < GL; ++i) fold(gx[m][i]);
+    } else {
+#pragma unroll 4
+      for (int64_t i = threadIdx.x; i < K8; i += 64 * kFW) fold(row4[m * K8 + i]);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, off)));
@@ -182,7 +229,7 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
   for (int m = 0; m < MR; ++m) {
     uint32_t mb = red_max[0][m];
 #pragma unroll
-    for (int w2 = 1; w2 < kWaves; ++w2) mb = max(mb, red_max[w2][m]);
+    for (int w2 = 1; w2 < kFW; ++w2) mb = max(mb, red_max[w2][m]);
     const bool bad = mb >= 0x7C00u;
     g[m] = bad ? __uint_as_float(0x7FC00000u) : half_bits_to_float(static_cast<uint16_t>(mb));
     zero[m] = bad || mb == 0u;
@@ -199,20 +246,14 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
     const int c1 = min(t1, c0 + kChunk);
     if (c0 != t0) {
       __syncthreads();                    // the previous chunk's planes are consumed
-      load_batch(c0, c1);
+      load_x(xq, c0, c1);                 // before the weights: see above
+#pragma unroll
+      for (int r = 0; r < kRing - 1; ++r) load_batch(w[r], c0 + r * kBatch, c1);
     }
-    // quantise tiles c0 + wave + 4j of this chunk into LDS (x loads issued together)
-    constexpr int kPerWave = kChunk / kWaves;
-    uint16_t xq[kPerWave][MR];
+    // quantise tiles c0 + wave + 4j of this chunk into LDS
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
-      const int tt = c0 + wave + kWaves * j;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) xq[j][m] = tt < c1 ? x[m * K + 64 * tt + koff] : uint16_t(0);
-    }
-#pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
-      const int tt = c0 + wave + kWaves * j;
+      const int tt = c0 + wave + kFW * j;
       if (tt < c1) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -233,28 +274,34 @@ __global__ __launch_bounds__(256) void gemv_fused_kernel(
     }
     __syncthreads();
     if (active) {
-      for (int tb = c0; tb < c1; tb += kBatch) {
-        u32x4 wc[kBatch];
+      // batch i of the chunk sits in ring slot i % kRing; batch i + kRing - 1 is issued
+      // (clamped, so unconditionally) before batch i is reduced
+      for (int tb = c0; tb < c1; tb += kRing * kBatch) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) wc[u] = w[u];
-        if (tb + kBatch < c1) load_batch(tb + kBatch, c1);
+        for (int r = 0; r < kRing; ++r) {
+          const int tr = tb + r * kBatch;
+          load_batch(w[(r + kRing - 1) % kRing], tr + (kRing - 1) * kBatch, c1);
+          if (tr < c1) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (tb + u < c1) {
+            for (int u = 0; u < kBatch; ++u) {
+              if (tr + u < c1) {
+                const u32x4 wc = w[r][u];
 #pragma unroll
-            for (int m = 0; m < MR; ++m) {
-              const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[tb + u - c0][m][0]);
-              const u32x4 p0 = X4[0], p1 = X4[1], p2 = X4[2], p3 = X4[3];
-              const uint32_t X[16] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
-                                      p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
+                for (int m = 0; m < MR; ++m) {
+                  const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[tr + u - c0][m][0]);
+                  const u32x4 p0 = X4[0], p1 = X4[1], p2 = X4[2], p3 = X4[3];
+                  const uint32_t X[16] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
+                                          p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
 #pragma unroll
-              for (int b = 0; b < 8; ++b) {
-                const uint32_t x0 = X[2 * b], x1 = X[2 * b + 1];
-                A[m][b] += __builtin_popcount((x0 & wc[u].x) | (~x0 & wc[u].z));
-                A[m][b] += __builtin_popcount((x1 & wc[u].y) | (~x1 & wc[u].w));
+                  for (int b = 0; b < 8; ++b) {
+                    const uint32_t x0 = X[2 * b], x1 = X[2 * b + 1];
+                    A[m][b] += __builtin_popcount((x0 & wc.x) | (~x0 & wc.z));
+                    A[m][b] += __builtin_popcount((x1 & wc.y) | (~x1 & wc.w));
+                  }
+                }
+                cn += __builtin_popcount(wc.z) + __builtin_popcount(wc.w);
               }
             }
-            cn += __builtin_popcount(wc[u].z) + __builtin_popcount(wc[u].w);
           }
         }
       }
@@ -284,9 +331,11 @@ struct GemvFusedPlan { int64_t groups, nsplit, tps; };
 
 GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
   const int64_t bands = N / 64;
-  const int64_t groups = (bands + kWaves - 1) / kWaves;
+  const int64_t groups = (bands + kFW - 1) / kFW;
   const int64_t KT = K / 64;
-  const int64_t target = g_gemvf_wg_target ? g_gemvf_wg_target : 768;   // measured on MI355X
+  // measured on MI355X: narrow outputs do best with fewer, longer workgroups (every
+  // workgroup reads the whole row for gamma), wide ones with more
+  const int64_t target = g_gemvf_wg_target ? g_gemvf_wg_target : (bands < 512 ? 256 : 512);
   int64_t nsplit = (target + groups / 2) / groups;
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kBatch));
   nsplit = std::max<int64_t>(nsplit, 1);
@@ -347,14 +396,25 @@ hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wp
   const GemvFusedPlan p = plan_gemv_fused(M, N, K);
   const dim3 grid(static_cast<unsigned>(p.groups), static_cast<unsigned>(p.nsplit));
   const u32x4* W = static_cast<const u32x4*>(wpacked);
-#define BL_GEMVF_LAUNCH(MR_)                                                                 \
-  hipLaunchKernelGGL(gemv_fused_kernel<MR_>, grid, dim3(256), 0, s, x, K, W, beta, beta_len, \
-                     N, y, ws_acc, ws_cnt, static_cast<int>(p.tps))
+#define BL_GEMVF_LAUNCH(MR_, GL_)                                                            \
+  hipLaunchKernelGGL((gemv_fused_kernel<MR_, GL_>), grid, dim3(64 * kFW), 0, s, x, K, W, beta, \
+                     beta_len, N, y, ws_acc, ws_cnt, static_cast<int>(p.tps))
+  // gamma loads unrolled per thread: K <= 512 kFW GL (row loads in registers); longer rows loop
+  const int64_t gl = (K / 8 + 64 * kFW - 1) / (64 * kFW);
   switch (M) {
-    case 1: BL_GEMVF_LAUNCH(1); break;
-    case 2: BL_GEMVF_LAUNCH(2); break;
-    case 3: BL_GEMVF_LAUNCH(3); break;
-    case 4: BL_GEMVF_LAUNCH(4); break;
+    case 1:
+      if (gl <= 4) BL_GEMVF_LAUNCH(1, 4);
+      else if (gl <= 8) BL_GEMVF_LAUNCH(1, 8);
+      else if (gl <= 16) BL_GEMVF_LAUNCH(1, 16);
+      else BL_GEMVF_LAUNCH(1, 0);
+      break;
+    case 2:
+      if (gl <= 4) BL_GEMVF_LAUNCH(2, 4);
+      else if (gl <= 8) BL_GEMVF_LAUNCH(2, 8);
+      else BL_GEMVF_LAUNCH(2, 0);
+      break;
+    case 3: BL_GEMVF_LAUNCH(3, 0); break;
+    case 4: BL_GEMVF_LAUNCH(4, 0); break;
     default: return hipErrorInvalidValue;
   }
 #undef BL_GEMVF_LAUNCH
