@@ -42,8 +42,6 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K);
 size_t onebit_part_floats(int64_t M, int64_t N, int64_t K);
 // fp32 split-K partials of the residual-binarisation forward for a shape.
 size_t residual_part_floats(int64_t M, int64_t N, int64_t K);
-// Number of output tiles (completion counters) the GEMM uses for a shape.
-int64_t gemm_max_tiles(int64_t M, int64_t N);
 
 // ---- launchers (all asynchronous on `s`) -----------------------------------------------
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
@@ -88,6 +86,10 @@ hipError_t launch_residual_linear(const uint16_t* x, const void* planes_o, const
                                   const void* planes_r, const float* alpha_r, int64_t M, int64_t N,
                                   int64_t K, float* y, float* ws_part, uint32_t* ws_cnt,
                                   hipStream_t s);
+// Weight-streaming ternary GEMM (int8 matrix cores, expansion in registers); M * K < 2^31.
+hipError_t launch_tern_mfma(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                            const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                            float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);

@@ -7,12 +7,13 @@
 //
 // Expansion: for a 32-input word, (X >> j) & 0x01010101 puts the flags of inputs 4j..4j+3
 // in bytes 0..3 (the layout's bit order was chosen for this), and
-// (P_bytes) + 255 * (N_bytes) turns flags into int8 +1 / -1 bytes in one v_mad_u32_u24.
+// (P_bytes) + 255 * (N_bytes) turns flags into int8 +1 / -1 bytes (expand_flags).
 //
 // Work split: a 256-thread workgroup owns a BM x BN output tile (4 waves, each a
 // (BM/WGM) x (BN/WGN) sub-tile of 16 x 16 MFMA fragments) and a range of 64-input k tiles.
-// Small-M shapes split K across workgroups; partial accumulators then meet in int32
-// atomics in the workspace and the last workgroup of a tile applies the epilogue.
+// This tiled kernel serves prefill (M > 64); batched decode (M <= 64) goes to the
+// weight-streaming kernel of tern_mfma.hip. When K is split across workgroups, partial
+// accumulators meet in the workspace's split words and the last one applies the epilogue.
 // Workgroup ids are remapped so that tiles sharing a weight column block run on the same
 // XCD (ids are dealt round-robin to the 8 XCDs), keeping that block in one L2.
 #include "bl_internal.h"
@@ -24,6 +25,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLd = 64 + 16;   // LDS row pitch in bytes (64 k per tile + pad)
+
+// Per byte: P flag -> 0x01 (+1), N flag -> 0xFF (-1), neither -> 0, i.e. pb + 255 nb. As
+// 32-bit arithmetic (pb - nb) + (nb << 8) equals it modulo 2^32 (the borrows cancel), so no
+// multiply is needed: one subtraction and one shift-and-add (written out because the
+// compiler folds the pair back into a 32-bit multiply).
+__device__ __forceinline__ uint32_t expand_flags(uint32_t pb, uint32_t nb) {
+  uint32_t o;
+  asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(o) : "v"(nb), "v"(pb - nb));
+  return o;
+}
 
 template <int BM, int BN, int WGM, int S>
 __global__ __launch_bounds__(256) void gemm_kernel(
@@ -37,7 +48,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   static_assert(FM >= 1 && FN >= 1, "tile too small");
   constexpr int A_CHUNKS = BM * 4;              // 16-byte chunks of an activation tile
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
-  constexpr int B_ITEMS = BN * 2;               // (row, half) expansion items
+  constexpr int B_ITEMS = BN * 4;               // (row, half, quarter) expansion items
   constexpr int B_PER = (B_ITEMS + 255) / 256;
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLd];
   __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLd];
@@ -61,24 +72,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   // Software pipeline: k tiles are fetched from global memory into registers S tiles ahead
   // of the one being multiplied, staged (weights expanded to int8) into one of two LDS
   // buffers, then multiplied; one barrier per k tile. The deep register prefetch hides
-  // the global-load latency, which is far longer than one tile's MFMA work.
+  // the global-load latency, which is far longer than one tile's MFMA work. Every fetch is
+  // unconditional (rows, columns, chunks and k tiles past their ranges are clamped into
+  // range; such values only reach outputs that are never stored): vector loads complete in
+  // issue order, and loads behind branches would make the compiler wait for all of them
+  // instead of for the one tile a step needs.
   u32x4 ra[S][A_PER];
   u32x4 rb[S][B_PER];
   auto fetch = [&](int s, int tk) {
+    tk = min(tk, t1 - 1);
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + 256 * i;
-      const int64_t row = m0 + (c >> 2);
-      ra[s][i] = u32x4{0, 0, 0, 0};
-      if (c < A_CHUNKS && row < M)
-        ra[s][i] = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + (c & 3) * 16);
+      const int c = min(tid + 256 * i, A_CHUNKS - 1);
+      const int64_t row = min<int64_t>(m0 + (c >> 2), M - 1);
+      ra[s][i] = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + (c & 3) * 16);
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + 256 * i;
-      const int64_t n = n0 + (c >> 1);
-      rb[s][i] = u32x4{0, 0, 0, 0};
-      if (c < B_ITEMS && n < N) rb[s][i] = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
+      const int c = min(tid + 256 * i, B_ITEMS - 1);
+      const int64_t n = min<int64_t>(n0 + (c >> 2), N - 1);
+      rb[s][i] = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
     }
   };
   auto stage = [&](int s, int buf) {
@@ -91,17 +104,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     for (int i = 0; i < B_PER; ++i) {
       const int c = tid + 256 * i;
       if (c < B_ITEMS) {
-        const int hh = c & 1;
+        // item c: tile row c / 4, half hh (inputs 32hh..), quarter qq (16 of those inputs)
+        const int hh = (c >> 1) & 1, qq = c & 1;
         const uint32_t P = hh ? rb[s][i].y : rb[s][i].x, Nm = hh ? rb[s][i].w : rb[s][i].z;
-        uint32_t o[8];
+        uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t pb = (P >> j) & 0x01010101u, nb = (Nm >> j) & 0x01010101u;
-          o[j] = pb + nb * 255u;                // +1 -> 0x01, -1 -> 0xFF per byte
+        for (int j = 0; j < 4; ++j) {
+          const int sh = 4 * qq + j;
+          const uint32_t pb = (P >> sh) & 0x01010101u, nb = (Nm >> sh) & 0x01010101u;
+          o[j] = expand_flags(pb, nb);
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(&Bs[buf][(c >> 1) * kLd + hh * 32]);
-        dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-        dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 2) * kLd + hh * 32 + qq * 16]) = u32x4{o[0], o[1], o[2], o[3]};
       }
     }
   };
@@ -112,31 +125,38 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
+  // Tile t sits in register slot (t - t0) % S and LDS buffer (t - t0) & 1. Each step
+  // multiplies the staged tile, then stages the next one into the other buffer (the
+  // matrix cores run while the VALU expands weights), refills the freed register slot and
+  // meets the other waves at one barrier.
+  auto compute = [&](int buf) {
+    i32x4 a[FM], b[FN];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-    if (t0 + s < t1) fetch(s, t0 + s);
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4)]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int s = 0; s < S; ++s) fetch(s, t0 + s);
+  stage(0, 0);
+  fetch(0, t0 + S);
+  __syncthreads();
   for (int kb = t0; kb < t1; kb += S) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int tk = kb + s;
-      if (tk < t1) {
-        const int buf = (tk - t0) & 1;
-        stage(s, buf);
-        if (tk + S < t1) fetch(s, tk + S);
-        __syncthreads();
-        i32x4 a[FM], b[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          a[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4)]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          b[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4)]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
+      const int ns = (s + 1) % S;
+      if (tk < t1) compute((tk - t0) & 1);
+      if (tk + 1 < t1) stage(ns, (tk + 1 - t0) & 1);
+      fetch(ns, tk + 1 + S);
+      if (tk < t1) __syncthreads();
     }
   }
   __syncthreads();
@@ -222,9 +242,9 @@ hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K
     case 15: return BL_TILES(64, 64, 2, 2);
     default: break;
   }
-  if (M <= 16) return BL_TILE(16, 128, 1);
-  if (M <= 32) return BL_TILE(32, 128, 2);
-  if (M <= 64) return BL_TILE(64, 128, 2);
+  // Batched decode: weights streamed into registers and expanded there (tern_mfma.hip);
+  // measured 1.1-2.2x faster than LDS tiles for M <= 64 on the 70B-shaped linears.
+  if (M <= 64) return launch_tern_mfma(q, gamma, M, K, wpacked, beta, beta_len, N, y, acc_out, ws_acc, s);
   // Prefill shapes are small next to 256 CUs (a 512 x 3200 output is 100 tiles of
   // 128 x 128): 64 x 64 tiles keep every CU busy; wide outputs take 64 x 128.
   const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
@@ -234,9 +254,5 @@ hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K
 #undef BL_TILES
 }
 
-int64_t gemm_max_tiles(int64_t M, int64_t N) {
-  const int64_t bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
-  return ((M + bm - 1) / bm) * ((N + 127) / 128);
-}
 
 }  // namespace bl

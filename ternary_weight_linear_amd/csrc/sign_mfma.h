@@ -206,7 +206,11 @@ __global__ __launch_bounds__(256) void sign_mfma_kernel(const SignMfmaArgs a) {
       if (j < n) {
         if (j + P - 1 < n)
           sign_load_tile<RES>(T[(d + P - 1) % P], a, L, band, m0, first + 4 * (j + P - 1), KT);
+        // keep the loads where they are: the scheduler would otherwise sink them towards
+        // their use and the tiles in flight would collapse to one
+        __builtin_amdgcn_sched_barrier(0);
         sign_compute_tile<RES>(T[d], acc, a.one);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

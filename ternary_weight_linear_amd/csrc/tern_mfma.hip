@@ -1,0 +1,257 @@
+// Ternary GEMM on int8 matrix cores with weights streamed straight into registers.
+//
+// [b158] "实验及结果": b1.58 models serve batches (Table 3, sequence length 512) and the
+// matrix product is an int8 accumulation (Fig. 3). acc[m, n] = sum_k q[m, k] w[n, k] with
+// q the int8 activations and w in {-1, 0, +1} from T2-PN-64, multiplied exactly by
+// v_mfma_i32_16x16x64_i8 (A = 16 rows of q, B = 16 weight rows expanded to int8).
+//
+// Expansion in registers: lane 16g + u needs, for weight row r = 16f + u of a 64-input tile,
+// the int8 values of inputs 16g .. 16g + 15. They sit in half h = g / 2 of the row's
+// T2-PN-64 words (P_h, N_h) at bit positions 8i + j with
+// j = 4(g % 2) .. 4(g % 2) + 3, so ((P_h >> j) & 0x01010101) gives the +1 flags of inputs
+// 4j .. 4j + 3 as bytes. Either flags_p + 255 flags_n (tern_expand) turns each word into
+// four int8 values for one MFMA, or the +1 and -1 flag bytes go to two MFMAs whose results
+// are subtracted.
+//
+// Mapping (the weight-streaming counterpart of the LDS-tiled GEMM, used for batched decode,
+// M <= 64, where the weights dominate the bytes): a workgroup of four waves owns one
+// 64-column band, FM 16-row tiles of q and a range of 64-input tiles. The waves take the
+// range's tiles in turn (wave w: tiles w, w + 4, ...) with kTernDepth - 1 tiles of loads in
+// flight (weights and q of a tile issued together, unconditionally: loads past a range are
+// clamped into it and never used), and meet in LDS with exact int32 sums. K splits across
+// workgroups meet in the 64-bit split words of the workspace (split_arrive), also exact.
+#include <algorithm>
+
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef BL_TERN_DEPTH
+#define BL_TERN_DEPTH 2
+#endif
+constexpr int kTernDepth = BL_TERN_DEPTH;   // tile sets per wave (depth - 1 in flight)
+
+__device__ __forceinline__ uint32_t tern_expand(uint32_t pb, uint32_t nb) {
+  // pb + 255 nb per byte as (pb - nb) + (nb << 8) (exact modulo 2^32: the borrows cancel);
+  // written out because the compiler folds the pair back into a 32-bit multiply
+  uint32_t o;
+  asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(o) : "v"(nb), "v"(pb - nb));
+  return o;
+}
+
+template <int FM>
+struct TernTile {
+  u32x4 w[4];            // T2-PN-64 row 16f + u of the tile: P0, P1, N0, N1; f = 0..3
+  u32x4 a[FM];           // q[m0 + 16fm + u, 64t + 16g .. +15]
+};
+
+struct TernArgs {
+  const int8_t* q;           // int8 [M, K]
+  const float* gamma;        // fp32 [M]
+  const u32x4* W;            // T2-PN-64 [N, K]
+  const float* beta;
+  int64_t beta_len, M, N, K;
+  float* y;                  // fp32 [M, N] (may be null)
+  int32_t* acc_out;          // int32 [M, N] (may be null)
+  uint64_t* ws_acc;          // split words [M, N] (nsplit > 1)
+  int tiles_per_split;
+};
+
+template <int FM>
+__device__ __forceinline__ void tern_load(TernTile<FM>& T, const TernArgs& a, int64_t band,
+                                          const uint32_t (&qoff)[FM], uint32_t woff, int t,
+                                          int KT) {
+  // woff = 16 u: row u of the tile (one 16-byte load per fragment; fewer, wider loads
+  // beat loading only the two words a lane uses)
+  const char* wt = reinterpret_cast<const char*>(a.W) + ((band * KT + t) << 10);
+#pragma unroll
+  for (int f = 0; f < 4; ++f) T.w[f] = *reinterpret_cast<const u32x4*>(wt + 256 * f + woff);
+  const char* qt = reinterpret_cast<const char*>(a.q) + static_cast<int64_t>(t) * 64;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) T.a[fm] = *reinterpret_cast<const u32x4*>(qt + qoff[fm]);
+}
+
+// SPLIT: multiply the +1 flags and the -1 flags separately (two MFMAs, acc = accP - accN,
+// four VALU ops per 16 weights); otherwise expand to int8 first (one MFMA, six VALU ops).
+// The first suits few rows of q (VALU-bound), the second many (matrix-core-bound).
+template <int FM, bool SPLIT>
+__device__ __forceinline__ void tern_compute(const TernTile<FM>& T, i32x4 (&acc)[FM][4],
+                                             i32x4 (&accn)[SPLIT ? FM : 1][4], const int (&js)[4],
+                                             bool hi) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const uint32_t Pw = hi ? T.w[f].y : T.w[f].x, Nw = hi ? T.w[f].w : T.w[f].z;
+    i32x4 bp, bn;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t pb = (Pw >> js[jj]) & 0x01010101u, nb = (Nw >> js[jj]) & 0x01010101u;
+      if constexpr (SPLIT) {
+        bp[jj] = static_cast<int>(pb);
+        bn[jj] = static_cast<int>(nb);
+      } else {
+        bp[jj] = static_cast<int>(tern_expand(pb, nb));
+      }
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const i32x4 av = __builtin_bit_cast(i32x4, T.a[fm]);
+      acc[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bp, acc[fm][f], 0, 0, 0);
+      if constexpr (SPLIT)
+        accn[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bn, accn[fm][f], 0, 0, 0);
+    }
+  }
+}
+
+template <int FM, bool SPLIT>
+__global__ __launch_bounds__(256) void tern_mfma_kernel(const TernArgs a) {
+  constexpr int P = kTernDepth;
+  constexpr int kRows = 16 * FM;
+  __shared__ int red[3][FM * 16][64];                   // waves 1..3, (fm, f, i), lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, u = lane & 15;
+  const int64_t band = blockIdx.x;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRows;
+  const int split = blockIdx.z, nsplit = gridDim.z;
+  const int KT = static_cast<int>(a.K / 64);
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(KT, t0 + a.tiles_per_split);
+  // q rows past M are clamped to row M - 1: they only reach outputs that are never stored
+  uint32_t qoff[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t row = min<int64_t>(m0 + 16 * fm + u, a.M - 1);
+    qoff[fm] = static_cast<uint32_t>(row * a.K + 16 * g);   // M*K < 2^31 (checked on the host)
+  }
+  const uint32_t woff = 16u * u;
+  const bool hi = g >= 2;                               // half h = g / 2 of the row
+  int js[4];                                            // bit offsets 4(g % 2) + jj
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) js[jj] = 4 * (g & 1) + jj;
+
+  i32x4 acc[FM][4], accn[SPLIT ? FM : 1][4];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[fm][f] = i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int fm = 0; fm < (SPLIT ? FM : 1); ++fm)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) accn[fm][f] = i32x4{0, 0, 0, 0};
+
+  // this wave's tiles: j = 0..n-1 at first + 4j; loads past the end are clamped to the last
+  const int first = t0 + wave;
+  const int n = first < t1 ? (t1 - first + 3) / 4 : 0;
+  const int last = n > 0 ? first + 4 * (n - 1) : t1 - 1;
+  TernTile<FM> T[P];
+#pragma unroll
+  for (int d = 0; d < P - 1; ++d) tern_load<FM>(T[d], a, band, qoff, woff, min(first + 4 * d, last), KT);
+  for (int j0 = 0; j0 < n; j0 += P) {
+#pragma unroll
+    for (int d = 0; d < P; ++d) {
+      const int j = j0 + d;
+      tern_load<FM>(T[(d + P - 1) % P], a, band, qoff, woff, min(first + 4 * (j + P - 1), last), KT);
+      // keep the loads where they are: the scheduler would otherwise sink them towards
+      // their use and the tiles in flight would collapse to one
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < n) tern_compute<FM, SPLIT>(T[d], acc, accn, js, hi);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[fm][f] -= accn[fm][f];
+  }
+
+  // waves 1..3 hand their sums to wave 0 through LDS (exact int32)
+  if (wave > 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][(fm * 4 + f) * 4 + i][lane] = acc[fm][f][i];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (fm * 4 + f) * 4 + i;
+        int v = acc[fm][f][i] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+        // D layout: lane l holds rows 4*(l/16) + i of the q tile, column l % 16 of fragment f
+        const int64_t row = m0 + 16 * fm + 4 * g + i;
+        const int64_t col = band * 64 + 16 * f + u;
+        if (row >= a.M) continue;
+        if (nsplit > 1 && !split_arrive(&a.ws_acc[row * a.N + col], v, nsplit, &v)) continue;
+        if (a.acc_out) a.acc_out[row * a.N + col] = v;
+        if (a.y)
+          a.y[row * a.N + col] = static_cast<float>(v) * (a.gamma[row] / 127.0f) *
+                                 a.beta[a.beta_len == 1 ? 0 : col];
+      }
+}
+
+struct TernPlan { int64_t bands, mgroups, nsplit, tps; int fm; bool split; };
+
+}  // namespace
+
+// Tuning knobs (harnesses that compile this file directly): workgroups to aim for, and a
+// fixed q rows per wave (16 FM); 0 = by shape.
+int64_t g_tern_wg_target = 0;
+int g_tern_fm = 0;
+int g_tern_split = -1;     // -1 by rows, 0 expand, 1 split
+
+namespace {
+
+TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
+  const int64_t KT = K / 64, bands = N / 64;
+  // measured on MI355X (70B-shaped decode at M = 8..64): one 16-row tile of q per wave
+  // (more workgroups, each weight tile re-read per 16 rows from L2) except for very wide
+  // outputs, where two
+  const int fm = g_tern_fm > 0 ? g_tern_fm : (M > 16 && bands >= 512 ? 2 : 1);
+  const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
+  const int64_t target = g_tern_wg_target > 0 ? g_tern_wg_target : 512;
+  int64_t nsplit = (target + bands * mgroups - 1) / (bands * mgroups);
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));   // >= 2 tiles per wave
+  nsplit = std::max<int64_t>(nsplit, 1);
+  if (M * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
+  nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
+  const int64_t tps = (KT + nsplit - 1) / nsplit;
+  const bool split = g_tern_split >= 0 ? g_tern_split == 1 : fm <= 2;   // VALU-bound at few rows
+  return {bands, mgroups, (KT + tps - 1) / tps, tps, fm, split};
+}
+
+}  // namespace
+
+hipError_t launch_tern_mfma(const int8_t* q, const float* gamma, int64_t M, int64_t K,
+                            const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
+                            float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
+  const TernPlan p = plan_tern(M, N, K);
+  TernArgs a{q, gamma, static_cast<const u32x4*>(wpacked), beta, beta_len, M, N, K, y, acc_out,
+             ws_acc, static_cast<int>(p.tps)};
+  const dim3 grid(static_cast<unsigned>(p.bands), static_cast<unsigned>(p.mgroups),
+                  static_cast<unsigned>(p.nsplit));
+#define BL_TERN_LAUNCH(FM_, SPLIT_) \
+  hipLaunchKernelGGL((tern_mfma_kernel<FM_, SPLIT_>), grid, dim3(256), 0, s, a)
+  switch (p.fm * 2 + (p.split ? 1 : 0)) {
+    case 2: BL_TERN_LAUNCH(1, false); break;
+    case 3: BL_TERN_LAUNCH(1, true); break;
+    case 4: BL_TERN_LAUNCH(2, false); break;
+    case 5: BL_TERN_LAUNCH(2, true); break;
+    case 9: BL_TERN_LAUNCH(4, true); break;
+    default: BL_TERN_LAUNCH(4, false); break;
+  }
+#undef BL_TERN_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace bl
