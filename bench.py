@@ -497,7 +497,7 @@ def main():
                    "launches_per_pass": main_res["launches_per_pass"],
                    "tokens_per_s": round(main_res["tokens_per_s"], 2),
                    "frac_hbm_peak": round(main_res["gbs"] / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_fused_kernel<1> (quantise + add-only GEMV)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_fused_kernel<1, GL> (quantise + add-only GEMV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
