@@ -388,6 +388,32 @@ def cpu_baseline(synth, budget_s=12.0):
             "host_cpus": os.cpu_count()}
 
 
+def bench_decode70b_stack(torch, tw, synth, dev, layers, M, steps, warmup):
+    """The same pass (M <= 4) as ONE persistent launch over all 320 linears
+    (bl_bitlinear_forward_stack): same activations, outputs and order as decode_pass, with a
+    grid-wide wait between consecutive linears."""
+    items, _, algo, wbytes, _ = decode_pass(torch, tw, synth, dev, layers, M)
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=dev)
+    plan = tw.bl_stack_prepare([(it["x"], it["w"], beta, it["y"]) for it in items], M)
+    count = len(items)
+    ws = tw.workspace(dev, tw.bl_workspace_bytes(M, 64, 128))
+    wsp, wsb = tw.ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    pp = tw.ctypes.c_void_p(plan.data_ptr())
+    lib = tw._lib
+
+    def full_pass():
+        st = lib.bl_bitlinear_forward_stack(pp, count, M, wsp, wsb,
+                                            tw.ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, tw._lib.bl_last_error()
+
+    ms = timed(torch, full_pass, steps, warmup)
+    status = tw.bl_stack_status(plan)
+    assert status == 0, f"stack status {status}"
+    return dict(ms_per_pass=ms, launches_per_pass=1, groups=count, algo_bytes=algo,
+                weight_bytes=wbytes, tokens_per_s=M / (ms / 1e3), gbs=algo / (ms / 1e3) / 1e9,
+                weight_gbs=wbytes / (ms / 1e3) / 1e9, graph=False, _plan=plan, _items=items)
+
+
 def gemv_traffic(launch_bytes):
     """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, or None if it
     is missing or was taken from a different gemv.hip."""
@@ -446,6 +472,10 @@ def main():
             M = int(args.only.split("_m")[1])
             res = bench_decode70b(torch, tw, synth, dev, layers, M, args.steps, args.warmup,
                                   use_graph=not args.no_graph)
+        elif args.only.startswith("stack_m"):
+            M = int(args.only.split("_m")[1])
+            res = bench_decode70b_stack(torch, tw, synth, dev, layers, M, args.steps, args.warmup)
+            res = {k: v for k, v in res.items() if not k.startswith("_")}
         print(json.dumps({args.only: res}))
         return
 

@@ -173,6 +173,58 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
                          const float* beta, int64_t beta_len, int64_t N, float* y, int path,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* ---- whole-stack decode in one launch ------------------------------------------------------- */
+
+/* One linear of a stack: y = BitLinear(x) exactly as bl_bitlinear_forward on the GEMV path
+ * computes it. x fp16 [M, K] (16-byte aligned), wpacked T2-PN-64 [N, K] (16-byte aligned),
+ * beta fp32 [beta_len] (1 or N), y fp32 [M, N]. N % 64 == 0, K % 64 == 0, K <= 65536. */
+typedef struct bl_linear_desc {
+  const uint16_t* x;
+  const void* wpacked;
+  const float* beta;
+  float* y;
+  int64_t beta_len;
+  int64_t N;
+  int64_t K;
+  int64_t reserved;  /* must be 0 */
+} bl_linear_desc;    /* 64 bytes */
+
+/* Bytes of the device plan for `count` linears: 64 + 64 * count. */
+size_t bl_stack_plan_bytes(int64_t count);
+
+/* Checks a list of linears and writes its device plan ("prepare once, call many", as the
+ * weights are). `linears` is a HOST array of `count` descriptors (1 <= count <= 4096);
+ * `plan` a device buffer of bl_stack_plan_bytes(count) bytes, 16-byte aligned, owned by the
+ * caller and read by every bl_bitlinear_forward_stack call that uses it. 1 <= M <= 4.
+ * Rejected (nothing queued): a y that overlaps any x of its own linear, any weight, beta,
+ * another linear's y or the plan (BL_ERR_ALIAS); shapes as above and M * N <= 4194304
+ * (BL_ERR_SHAPE). A y that overlaps the x of a LATER linear is allowed: that linear then
+ * reads what the earlier one wrote. The plan records which linears read an earlier output.
+ * Blocks until the plan is on the device (a synchronous copy on `stream`). */
+int bl_stack_prepare(const bl_linear_desc* linears, int64_t count, int64_t M, void* plan,
+                     size_t plan_bytes, void* stream);
+
+/* Decode a whole stack of BitLinear layers in ONE persistent launch ([b158] "实验及结果",
+ * Table 3: the 70B model's decode throughput is a sweep over all its linears; Fig. 3: each
+ * product is int8 additions). The result is bit-identical to calling bl_bitlinear_forward
+ * (GEMV path) for linears 0 .. count-1 in order on one stream: linear l reads its x only
+ * after linears 0 .. l-1 have written their y (a grid-wide wait between consecutive
+ * linears), while the weights of the next linear are already being read during that wait.
+ * count and M must be the values the plan was prepared with. Uses ws: any workspace of
+ * bl_workspace_bytes(M, N, K) bytes for some N, K is large enough; zero-filled before its
+ * first use and left zero. The launch needs every one of its workgroups resident at once
+ * (a cooperative launch; it fails with BL_ERR_HIP if the device cannot hold them); the
+ * environment variable BL_STACK_GRID = n > 0 caps the grid at n workgroups. Device
+ * status, read with bl_stack_status: 0 ok; 1 the plan header does not match count / M
+ * (nothing computed); 2 a grid-wide wait exceeded about two seconds (outputs undefined;
+ * clear the workspace before reusing it). */
+int bl_bitlinear_forward_stack(const void* plan, int64_t count, int64_t M, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Synchronises `stream` and returns the device status word of `plan` (see above; it stays
+ * set until the plan is prepared again), or a negative value if it cannot be read. */
+int bl_stack_status(const void* plan, void* stream);
+
 /* ---- OneBit forward ------------------------------------------------------------------------ */
 
 /* OneBit linear ([onebit] "1. 新的1bit结构", Fig. 3): y = ((x ⊙ g) · S^T) ⊙ h with

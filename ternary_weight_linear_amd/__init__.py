@@ -58,7 +58,17 @@ _SIGS = {
     "bl_svid_rank1": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
     "bl_residual_binarize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "bl_residual_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "bl_stack_plan_bytes": (_SZ, [_I64]),
+    "bl_stack_prepare": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
+    "bl_bitlinear_forward_stack": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
+    "bl_stack_status": (ctypes.c_int, [_P, _P]),
 }
+
+
+class bl_linear_desc(ctypes.Structure):
+    """One linear of a stack plan (the C struct of the same name)."""
+    _fields_ = [("x", _P), ("wpacked", _P), ("beta", _P), ("y", _P),
+                ("beta_len", _I64), ("N", _I64), ("K", _I64), ("reserved", _I64)]
 
 
 def header_functions(path: str = HEADER_PATH):
@@ -370,6 +380,61 @@ def bl_residual_linear(x, planes_o, alpha_o, planes_r, alpha_r, out=None):
                                    _ptr(alpha_r), M, N, K, _ptr(y), _ptr(ws), wsb, _stream(d)),
            "bl_residual_linear")
     return y
+
+
+def bl_stack_plan_bytes(count: int) -> int:
+    return _lib.bl_stack_plan_bytes(count)
+
+
+def bl_stack_prepare(linears, M: int, descs_only: bool = False):
+    """Device plan (uint8 tensor) for a list of linears, each a tuple
+    (x fp16 [M, K], wpacked uint8 T2-PN-64, beta fp32 [1] or [N], y fp32 [M, N]).
+    The plan keeps raw pointers: the tensors must stay alive (and in place) while it is used.
+    descs_only=True returns the ctypes descriptor array instead (no device work)."""
+    if not linears:
+        raise ValueError("a stack needs at least one linear")
+    arr = (bl_linear_desc * len(linears))()
+    tensors = []
+    for i, (x, wpacked, beta, y) in enumerate(linears):
+        _half_bits(x, f"linears[{i}].x")
+        _need(wpacked, torch.uint8, f"linears[{i}].wpacked")
+        _need(beta, torch.float32, f"linears[{i}].beta")
+        _need(y, torch.float32, f"linears[{i}].y")
+        if x.dim() != 2 or y.dim() != 2 or x.shape[0] != M or y.shape[0] != M:
+            raise ValueError(f"linears[{i}]: x and y must be [M, *] with M = {M}")
+        N, K = y.shape[1], x.shape[1]
+        arr[i] = bl_linear_desc(x.data_ptr(), wpacked.data_ptr(), beta.data_ptr(), y.data_ptr(),
+                                _beta_len(beta, N), N, K, 0)
+        tensors += [x, wpacked, beta, y]
+    if descs_only:
+        return arr
+    d = _dev(*tensors)
+    nbytes = _lib.bl_stack_plan_bytes(len(linears))
+    if nbytes == 0:
+        raise ValueError(f"a stack holds 1 .. 4096 linears, got {len(linears)}")
+    plan = torch.empty(nbytes, dtype=torch.uint8, device=d)
+    _check(_lib.bl_stack_prepare(ctypes.cast(arr, _P), len(linears), M, _ptr(plan), nbytes,
+                                 _stream(d)), "bl_stack_prepare")
+    return plan
+
+
+def bl_bitlinear_forward_stack(plan, count: int, M: int):
+    """Run every linear of `plan` in order in one persistent launch (outputs land in the
+    y tensors the plan was prepared with)."""
+    _need(plan, torch.uint8, "plan")
+    d = _dev(plan)
+    ws, wsb = _ws_for(d, M, 64, 128)
+    _check(_lib.bl_bitlinear_forward_stack(_ptr(plan), count, M, _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_forward_stack")
+
+
+def bl_stack_status(plan) -> int:
+    """Device status word of a plan (synchronises the current stream)."""
+    d = _dev(plan)
+    st = _lib.bl_stack_status(_ptr(plan), _stream(d))
+    if st < 0:
+        raise BitLinearError(6, "bl_stack_status", _lib)
+    return st
 
 
 __all__ = [n for n in list(globals()) if n.startswith("bl_")] + [

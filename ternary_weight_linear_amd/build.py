@@ -32,6 +32,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-result"]
 
 SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "onebit.hip", "svid.hip",
+           "stack.hip",
            "residual.hip", "tern_mfma.hip"]
 
 

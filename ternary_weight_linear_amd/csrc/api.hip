@@ -35,6 +35,7 @@ inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxMtiles = 65535;     // 16-row tiles of x along the grid's y dimension
 constexpr int64_t kMaxSignK = int64_t(1) << 26;   // fp16-input kernels use 32-bit row offsets
+constexpr int64_t kMaxStack = 4096;               // linears in one stack plan
 
 inline bool dims_ok(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && N >= 1 && K >= 1 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
@@ -323,6 +324,72 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
     e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, wscnt, s);
   }
   return check_launch(e, "bl_bitlinear_forward");
+}
+
+size_t bl_stack_plan_bytes(int64_t count) {
+  return count >= 1 && count <= kMaxStack ? stack_plan_bytes(count) : 0;
+}
+
+int bl_stack_prepare(const bl_linear_desc* linears, int64_t count, int64_t M, void* plan,
+                     size_t plan_bytes, void* stream) {
+  if (!linears || !plan) return BL_ERR_NULL;
+  if (count < 1 || count > kMaxStack || M < 1 || M > 4) return BL_ERR_SHAPE;
+  if (plan_bytes < stack_plan_bytes(count)) return BL_ERR_ARG;
+  if (!aligned16(plan)) return BL_ERR_ALIGN;
+  const size_t pb = stack_plan_bytes(count);
+  for (int64_t l = 0; l < count; ++l) {
+    const bl_linear_desc& d = linears[l];
+    if (!d.x || !d.wpacked || !d.beta || !d.y) return BL_ERR_NULL;
+    if (!dims_ok(M, d.N, d.K) || d.N % 64 || d.K % 64 || d.K > 65536 || M * d.N > kAccCap)
+      return BL_ERR_SHAPE;
+    const int st = check_beta(d.beta, d.beta_len, d.N);
+    if (st) return st;
+    if (d.reserved != 0) return BL_ERR_ARG;
+    if (!aligned16(d.x) || !aligned16(d.wpacked)) return BL_ERR_ALIGN;
+  }
+  for (int64_t l = 0; l < count; ++l) {
+    const bl_linear_desc& d = linears[l];
+    const size_t yb = static_cast<size_t>(M * d.N) * 4;
+    if (overlap(d.y, yb, d.x, static_cast<size_t>(M * d.K) * 2) || overlap(d.y, yb, plan, pb))
+      return BL_ERR_ALIAS;
+    for (int64_t j = 0; j < count; ++j) {
+      const bl_linear_desc& o = linears[j];
+      if (overlap(d.y, yb, o.wpacked, static_cast<size_t>(o.N * o.K / 4)) ||
+          overlap(d.y, yb, o.beta, static_cast<size_t>(o.beta_len) * 4) ||
+          (j != l && overlap(d.y, yb, o.y, static_cast<size_t>(M * o.N) * 4)))
+        return BL_ERR_ALIAS;
+    }
+  }
+  return check_launch(stack_write_plan(linears, count, M, plan, static_cast<hipStream_t>(stream)),
+                      "bl_stack_prepare");
+}
+
+int bl_bitlinear_forward_stack(const void* plan, int64_t count, int64_t M, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!plan) return BL_ERR_NULL;
+  if (count < 1 || count > kMaxStack || M < 1 || M > 4) return BL_ERR_SHAPE;
+  if (!aligned16(plan)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, 64, 128);
+  if (!ws || ws_bytes < L.acc_off + L.acc_bytes) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  char* w = static_cast<char*>(ws);
+  auto* wsacc = reinterpret_cast<uint64_t*>(w + L.acc_off);
+  // the grid-wide wait uses the last words of the (zero-maintained) counter region
+  auto* bar = reinterpret_cast<uint32_t*>(w + L.cnt_off) + (kMaxCounters - stack_barrier_words());
+  return check_launch(launch_gemv_stack(plan, count, M, bar, wsacc,
+                                        static_cast<hipStream_t>(stream)),
+                      "bl_bitlinear_forward_stack");
+}
+
+int bl_stack_status(const void* plan, void* stream) {
+  if (!plan) return -1;
+  uint32_t st = 0;
+  const hipError_t e = stack_read_status(plan, &st, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    hip_fail(e, "bl_stack_status");
+    return -1;
+  }
+  return static_cast<int>(st);
 }
 
 int bl_svid_rank1(const float* W, int64_t N, int64_t K, int iters, void* spacked, uint16_t* g,

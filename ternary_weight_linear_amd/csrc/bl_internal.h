@@ -90,6 +90,15 @@ hipError_t launch_residual_linear(const uint16_t* x, const void* planes_o, const
 hipError_t launch_tern_mfma(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                             const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                             float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s);
+// Whole-stack decode (stack.hip): the device plan of a list of linears, its persistent
+// launch (barrier = a zero-maintained counter, ws_acc the split words) and its status word.
+size_t stack_plan_bytes(int64_t count);
+hipError_t stack_write_plan(const bl_linear_desc* linears, int64_t count, int64_t M, void* plan,
+                            hipStream_t s);
+hipError_t launch_gemv_stack(const void* plan, int64_t count, int64_t M, uint32_t* bar,
+                             uint64_t* ws_acc, hipStream_t s);
+size_t stack_barrier_words();   // zero-maintained uint32 words of the grid-wide wait
+hipError_t stack_read_status(const void* plan, uint32_t* status, hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);

@@ -143,3 +143,57 @@ def test_residual_checks(lib):
     assert lin(y=_p(D + 4096)) == ALIAS
     assert lib.bl_onebit_linear(_p(A + 8), _p(A + 4096), _p(B), _p(B + 8192), 1, 64, 128, _p(C), _p(D),
                                 lib.bl_workspace_bytes(1, 64, 128), None) == ALIGN
+
+
+def test_stack_checks(lib):
+    import ternary_weight_linear_amd as tw
+    assert lib.bl_stack_plan_bytes(320) == 64 + 64 * 320
+    assert lib.bl_stack_plan_bytes(0) == 0 and lib.bl_stack_plan_bytes(4097) == 0
+    M = 2
+    # two linears: [1024 x 512] then [256 x 1024]; buffers at distinct fake addresses
+    shapes = [(1024, 512), (256, 1024)]
+
+    def descs(over=None):
+        arr = (tw.bl_linear_desc * 2)()
+        for i, (N, K) in enumerate(shapes):
+            arr[i] = tw.bl_linear_desc(A + i * 0x100000, B + i * 0x1000000, C + i * 0x1000,
+                                       D + i * 0x100000, 1, N, K, 0)
+        for (i, f), v in (over or {}).items():
+            setattr(arr[i], f, v)
+        return arr
+
+    plan = D + 0x10000000
+    pb = lib.bl_stack_plan_bytes(2)
+
+    def prep(arr, count=2, m=M, p=plan, nbytes=pb):
+        return lib.bl_stack_prepare(ctypes.cast(arr, ctypes.c_void_p), count, m, _p(p), nbytes, None)
+
+    assert lib.bl_stack_prepare(None, 2, M, _p(plan), pb, None) == NULL
+    assert prep(descs(), p=0) == NULL
+    assert prep(descs({(1, "beta"): None})) == NULL
+    assert prep(descs(), count=0) == SHAPE
+    assert prep(descs(), count=4097) == SHAPE
+    assert prep(descs(), m=5) == SHAPE
+    assert prep(descs(), nbytes=pb - 1) == ARG
+    assert prep(descs(), p=plan + 8) == ALIGN
+    assert prep(descs({(0, "N"): 100})) == SHAPE                 # N % 64
+    assert prep(descs({(1, "K"): 65536 + 64})) == SHAPE          # K > 65536
+    assert prep(descs({(0, "N"): 4194304, (0, "y"): 0x200000000})) == SHAPE   # M * N > 2^22
+    assert prep(descs({(1, "beta_len"): 7})) == ARG
+    assert prep(descs({(0, "reserved"): 1})) == ARG
+    assert prep(descs({(0, "x"): A + 2})) == ALIGN
+    assert prep(descs({(1, "wpacked"): B + 8})) == ALIGN
+    assert prep(descs({(0, "y"): A + 512})) == ALIAS              # y over its own x
+    assert prep(descs({(1, "y"): B + 64})) == ALIAS               # y over a weight
+    assert prep(descs({(0, "y"): C + 0x1000})) == ALIAS           # y over another beta
+    assert prep(descs({(1, "y"): D + 1024})) == ALIAS             # y over another y
+    assert prep(descs({(0, "y"): plan - 4096})) == ALIAS          # y over the plan
+    wsb = lib.bl_workspace_bytes(M, 64, 128)
+    assert lib.bl_bitlinear_forward_stack(None, 2, M, _p(A), wsb, None) == NULL
+    assert lib.bl_bitlinear_forward_stack(_p(plan), 0, M, _p(A), wsb, None) == SHAPE
+    assert lib.bl_bitlinear_forward_stack(_p(plan), 2, 0, _p(A), wsb, None) == SHAPE
+    assert lib.bl_bitlinear_forward_stack(_p(plan + 4), 2, M, _p(A), wsb, None) == ALIGN
+    assert lib.bl_bitlinear_forward_stack(_p(plan), 2, M, None, wsb, None) == WS
+    assert lib.bl_bitlinear_forward_stack(_p(plan), 2, M, _p(A), 4096, None) == WS
+    assert lib.bl_bitlinear_forward_stack(_p(plan), 2, M, _p(A + 16), wsb, None) == ALIGN
+    assert lib.bl_stack_status(None, None) < 0

@@ -109,3 +109,27 @@ def test_stack_layer_graph_replays_match_eager(layer0):
         tmp = torch.randn(1 << 20, device=DEV).sum()       # eager work between replays
         torch.cuda.synchronize()
         del tmp
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_stack_kernel_full_size(layer0, M):
+    """The persistent whole-stack launch (the benchmark's launch configuration) on the 70B
+    layer's four groups three times over (12 linears): every output bitwise equal to one
+    bl_bitlinear_forward call per linear, sampled rows against the oracle."""
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
+    lins = []
+    for rep in range(3):
+        for gi, (gname, buf, N, K, parts) in enumerate(layer0):
+            x16 = synth.normal_fp16((M, K), 0, 5, 3000 + rep, gi)
+            y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+            lins.append((gname, x16, torch.from_numpy(x16).to(DEV), buf, N, K, parts, y))
+    say("fullsize stack kernel M", M, "linears", len(lins))
+    plan = tw.bl_stack_prepare([(x, buf, beta, y) for _, _, x, buf, _, _, _, y in lins], M)
+    tw.bl_bitlinear_forward_stack(plan, len(lins), M)
+    assert tw.bl_stack_status(plan) == 0
+    for i, (gname, x16, x, buf, N, K, parts, y) in enumerate(lins):
+        ref = tw.bl_bitlinear_forward(x, buf, beta, N, path=tw.BL_PATH_GEMV)
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), f"linear {i} ({gname})"
+        if i < 4:
+            ids, yref = _sampled_reference(x16, parts, K, 16, seed=100 + i + 10 * M)
+            assert_rel(host(y)[:, ids], yref)

@@ -412,3 +412,159 @@ def test_workspace_left_zero():
     zero_prefix = 65536 * 4 + 64 * 65536 * 8        # counters + split-K words
     for d, buf in tw._ws.items():
         assert not host(buf[:zero_prefix]).any(), "zero-maintained workspace left dirty"
+
+
+# ----------------------------------------------------------------------------- whole-stack decode
+# Shapes that exercise the work split: one band (N = 64), band counts not a multiple of four,
+# one 64-input tile (K = 64), an odd tile count (K = 4160), few groups with long rows (more
+# workgroups than group tiles, many workgroups per group), and a wide output.
+STACK_SHAPES = [(64, 64), (192, 320), (512, 512), (320, 1024), (1024, 256), (64, 8192),
+                (256, 4160), (4096, 1024)]
+
+
+def _stack_linears(shapes, M, seed):
+    """Per linear: host codes, packed weights, beta (scalar or per row), x, y buffer."""
+    out = []
+    for i, (N, K) in enumerate(shapes):
+        codes = synth.ternary_codes(synth.matrix_key(seed, 120, i, N), N, K)
+        if i % 2:
+            beta = synth.uniform_fp16((N,), 0.01, 0.03, seed, 121, i).astype(np.float32)
+        else:
+            beta = np.array([synth.BETA_DIRECT], np.float32)
+        x = synth.normal_fp16((M, K), seed, 122, i, M)
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        out.append(dict(codes=codes, packed=tw.bl_pack_ternary(dev(codes)), beta=beta,
+                        dbeta=dev(beta), x=x, dx=dev(x), y=y, N=N, K=K))
+    return out
+
+
+def _stack_oracle(l):
+    yref, _, _, _ = oracle.bitlinear_forward(l["x"], l["codes"], l["beta"])
+    return yref
+
+
+def _run_stack(lins, M):
+    plan = tw.bl_stack_prepare([(l["dx"], l["packed"], l["dbeta"], l["y"]) for l in lins], M)
+    tw.bl_bitlinear_forward_stack(plan, len(lins), M)
+    return plan
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_stack_matches_oracle(M):
+    say("stack vs oracle", M)
+    lins = _stack_linears(STACK_SHAPES, M, seed=M)
+    plan = _run_stack(lins, M)
+    assert tw.bl_stack_status(plan) == 0
+    for l in lins:
+        assert_rel(host(l["y"]), _stack_oracle(l))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_stack_equals_separate_calls(M):
+    """One persistent launch gives the bits of bl_bitlinear_forward (GEMV path) per linear,
+    and repeated launches give the same bits."""
+    say("stack vs separate", M)
+    lins = _stack_linears(STACK_SHAPES, M, seed=10 + M)
+    plan = _run_stack(lins, M)
+    first = [host(l["y"]).view(np.uint32).copy() for l in lins]
+    for l, f in zip(lins, first):
+        y = tw.bl_bitlinear_forward(l["dx"], l["packed"], l["dbeta"], l["N"], path=tw.BL_PATH_GEMV)
+        assert np.array_equal(host(y).view(np.uint32), f)
+    for l in lins:
+        l["y"].fill_(float("nan"))
+    tw.bl_bitlinear_forward_stack(plan, len(lins), M)
+    for l, f in zip(lins, first):
+        assert np.array_equal(host(l["y"]).view(np.uint32), f)
+    assert tw.bl_stack_status(plan) == 0
+
+
+@pytest.mark.parametrize("grid", [1, 3, 8, 37, 300])
+def test_stack_small_grids(grid, monkeypatch):
+    """Capped grids: workgroups whose share spans several groups and several 64-tile chunks
+    (512 x 32768 at 8 workgroups: 128 tiles per share), linears a workgroup has no part of."""
+    say("stack grid", grid)
+    monkeypatch.setenv("BL_STACK_GRID", str(grid))
+    lins = _stack_linears([(512, 32768), (192, 320), (64, 64), (1024, 2048)], 1, seed=20 + grid)
+    plan = _run_stack(lins, 1)
+    assert tw.bl_stack_status(plan) == 0
+    for l in lins:
+        assert_rel(host(l["y"]), _stack_oracle(l))
+
+
+def test_stack_read_after_write_and_write_after_read():
+    """Linear 1 reads, as its fp16 x, the bytes linear 0 writes as fp32 y; linear 2 writes
+    its y over linear 0's x. The stack must give the bits of three calls in order."""
+    say("stack hazards")
+    N0, K0, N1, N2, K2 = 256, 512, 128, 256, 256
+    c0 = synth.ternary_codes(synth.matrix_key(0, 123, 0, 0), N0, K0)
+    c1 = synth.ternary_codes(synth.matrix_key(0, 123, 1, 0), N1, 2 * N0)
+    c2 = synth.ternary_codes(synth.matrix_key(0, 123, 2, 0), N2, K2)
+    p0, p1, p2 = (tw.bl_pack_ternary(dev(c)) for c in (c0, c1, c2))
+    # x0: a few entries of +-127, so gamma = 127, q = x0 and y0 = acc (beta = 1) are small
+    # integers whose fp32 bit patterns read as finite fp16 pairs
+    x0 = np.zeros((1, K0), np.float16)
+    x0[0, [3, 100, 257, 511]] = [127, -127, 127, 127]
+    one = dev(np.array([1.0], np.float32))
+    b1 = dev(synth.uniform_fp16((N1,), 0.01, 0.03, 0, 124, 1).astype(np.float32))
+    b2 = dev(np.array([0.25], np.float32))
+    x2 = synth.normal_fp16((1, K2), 0, 125, 2)
+
+    def buffers():
+        buf0 = torch.full((1, N0), float("nan"), dtype=torch.float32, device=DEV)  # y0 = x1
+        xb0 = dev(x0)                                                                # x0 = y2
+        y1 = torch.full((1, N1), float("nan"), dtype=torch.float32, device=DEV)
+        return buf0, xb0, y1
+
+    # separate calls in order
+    r0, rx0, ry1 = buffers()
+    r0.copy_(tw.bl_bitlinear_forward(rx0, p0, one, N0, path=tw.BL_PATH_GEMV))
+    ry1.copy_(tw.bl_bitlinear_forward(r0.view(torch.float16), p1, b1, N1, path=tw.BL_PATH_GEMV))
+    rx0.view(torch.float32).copy_(tw.bl_bitlinear_forward(dev(x2), p2, b2, N2, path=tw.BL_PATH_GEMV))
+    # one stack
+    s0, sx0, sy1 = buffers()
+    dx2 = dev(x2)
+    plan = tw.bl_stack_prepare([(sx0, p0, one, s0), (s0.view(torch.float16), p1, b1, sy1),
+                                (dx2, p2, b2, sx0.view(torch.float32))], 1)
+    tw.bl_bitlinear_forward_stack(plan, 3, 1)
+    assert tw.bl_stack_status(plan) == 0
+    for a, b in ((r0, s0), (ry1, sy1), (rx0, sx0)):
+        assert np.array_equal(host(a).view(np.uint16), host(b).view(np.uint16))
+    # and against the oracle: y0 is exact, x1 is the fp16 reading of y0's bytes
+    acc0 = oracle.acc_exact(x0.astype(np.int8), c0)
+    assert np.array_equal(host(s0), acc0.astype(np.float32))
+    x1 = host(s0).view(np.float16)
+    assert np.isfinite(x1).all()
+    y1ref, _, _, _ = oracle.bitlinear_forward(x1, c1, host(b1))
+    assert_rel(host(sy1), y1ref)
+    y2ref, _, _, _ = oracle.bitlinear_forward(x2, c2, np.float32(0.25))
+    assert_rel(host(sx0).view(np.float32), y2ref)
+
+
+def test_stack_plan_mismatch_sets_status():
+    """A launch whose count or M differs from the plan's computes nothing and sets status 1;
+    preparing the plan again clears it."""
+    say("stack mismatch")
+    lins = _stack_linears([(128, 256), (64, 128)], 1, seed=30)
+    descs = [(l["dx"], l["packed"], l["dbeta"], l["y"]) for l in lins]
+    plan = tw.bl_stack_prepare(descs, 1)
+    tw.bl_bitlinear_forward_stack(plan, 3, 1)
+    assert tw.bl_stack_status(plan) == 1
+    assert all(torch.isnan(l["y"]).all() for l in lins)
+    plan2 = tw.bl_stack_prepare(descs, 1)
+    tw.bl_bitlinear_forward_stack(plan2, 2, 2)
+    assert tw.bl_stack_status(plan2) == 1
+    plan3 = tw.bl_stack_prepare(descs, 1)
+    tw.bl_bitlinear_forward_stack(plan3, 2, 1)
+    assert tw.bl_stack_status(plan3) == 0
+    for l in lins:
+        assert_rel(host(l["y"]), _stack_oracle(l))
+
+
+def test_stack_leaves_workspace_zero():
+    say("stack workspace zero")
+    lins = _stack_linears(STACK_SHAPES[:5], 2, seed=31)
+    _run_stack(lins, 2)
+    torch.cuda.synchronize()
+    zero_prefix = 65536 * 4 + 64 * 65536 * 8        # counters (incl. the arrival counter) + split words
+    for d, buf in tw._ws.items():
+        assert not host(buf[:zero_prefix]).any(), "zero-maintained workspace left dirty"
