@@ -483,6 +483,10 @@ def main():
                                use_graph=not args.no_graph)
     log("decode70b M=1:", json.dumps(main_res))
     if not args.skip_extra:
+        r = bench_decode70b_stack(torch, tw, synth, dev, layers, 1, args.steps, args.warmup)
+        extra["decode70b_m1_stack"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs", "launches_per_pass")}
+        del r
+        log("decode70b M=1, one persistent launch:", json.dumps(extra["decode70b_m1_stack"]))
         for M in (8, 32, 64):
             r = bench_decode70b(torch, tw, synth, dev, layers, M, max(3, args.steps // 4), 1,
                                 use_graph=not args.no_graph)
