@@ -108,6 +108,15 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// popcount(x) + acc in one v_bcnt_u32_b32 (its second operand accumulates). Written out:
+// the compiler sums pairs of popcounts with a three-input add instead, one more VALU op
+// per pair in the add-only loops.
+__device__ __forceinline__ uint32_t bcnt_acc(uint32_t x, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+  return r;
+}
+
 // Split-K hand-off between workgroups without cache write-back fences.
 // Partial results move only through agent-scope atomics, which the hardware performs at
 // the device-wide coherence point rather than in one XCD's L2, so no L2 write-back or

@@ -70,11 +70,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
             const uint32_t x0 = X[2 * b], x1 = X[2 * b + 1];
-            A[m][b] += __builtin_popcount((x0 & w[u].x) | (~x0 & w[u].z));
-            A[m][b] += __builtin_popcount((x1 & w[u].y) | (~x1 & w[u].w));
+            A[m][b] = static_cast<int>(bcnt_acc((x0 & w[u].x) | (~x0 & w[u].z), static_cast<uint32_t>(A[m][b])));
+            A[m][b] = static_cast<int>(bcnt_acc((x1 & w[u].y) | (~x1 & w[u].w), static_cast<uint32_t>(A[m][b])));
           }
         }
-        cn += __builtin_popcount(w[u].z) + __builtin_popcount(w[u].w);
+        cn = static_cast<int>(bcnt_acc(w[u].w, bcnt_acc(w[u].z, static_cast<uint32_t>(cn))));
       }
     }
   }
@@ -295,11 +295,11 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
 #pragma unroll
                   for (int b = 0; b < 8; ++b) {
                     const uint32_t x0 = X[2 * b], x1 = X[2 * b + 1];
-                    A[m][b] += __builtin_popcount((x0 & wc.x) | (~x0 & wc.z));
-                    A[m][b] += __builtin_popcount((x1 & wc.y) | (~x1 & wc.w));
+                    A[m][b] = static_cast<int>(bcnt_acc((x0 & wc.x) | (~x0 & wc.z), static_cast<uint32_t>(A[m][b])));
+                    A[m][b] = static_cast<int>(bcnt_acc((x1 & wc.y) | (~x1 & wc.w), static_cast<uint32_t>(A[m][b])));
                   }
                 }
-                cn += __builtin_popcount(wc.z) + __builtin_popcount(wc.w);
+                cn = static_cast<int>(bcnt_acc(wc.w, bcnt_acc(wc.z, static_cast<uint32_t>(cn))));
               }
             }
           }
