@@ -18,11 +18,12 @@ definition, no blocking or fusion. Sources, cited by page title and section:
   blog summary, sections "方法细节" (step 2, residual approximation) and
   "存储位开销分析".
 
-Readings taken where the pages are silent are stated in each function and
-listed in the design doc. Parity status of each function is in its docstring.
+Readings taken where the pages are silent are stated in each function. Parity status
+of each function is in its docstring.
 """
-from .formats import (pack_ternary, unpack_ternary, pack_sign, unpack_sign, act_planes,
-                      ternary_packed_bytes, sign_packed_bytes)
+from .formats import (pack_ternary, unpack_ternary, pack_ternary_mf, unpack_ternary_mf,
+                      pack_sign, unpack_sign, act_planes, ternary_packed_bytes,
+                      sign_packed_bytes)
 from .b158 import (QB, exact_abs_sum, f32_nearest, absmean_beta, ternarize_absmean,
                    quant_act_int8, acc_exact, bitlinear_output, bitlinear_forward)
 from .onebit import (onebit_forward, onebit_error_scale, onebit_storage_bits,

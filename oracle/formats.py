@@ -20,6 +20,12 @@ X8-64 (activation bit planes of int8 q, used by the add-only GEMV).
   Word 2b + h holds bit b (two's complement, b = 0..7) of q[m, 64t + 32h + c],
   with c = 4j + i at bit 8i + j, the same order as T2-PN-64.
 
+T2-MF64 (ternary, 2 bits/weight, for int8 matrix-core operands). N % 64 == 0,
+  K % 64 == 0. Tiles as T2-PN-64 (64 rows x 64 inputs, 1024 bytes, same order), read
+  as 256 little-endian uint32 words. Tile row r = 16f + u (f, u: 0..3, 0..15) and tile
+  input c = 16g + 4j + i (g, j, i: 0..3) sit in word 4*(16g + u) + f at bits 8i + 2j
+  and 8i + 2j + 1, holding the code w + 1 (0, 1, 2; 3 is invalid).
+
 S1-128 (sign, 1 bit/weight). N % 64 == 0, K % 128 == 0.
   Tile (tn, tk) = rows 64tn.., inputs 128tk.., 1024 bytes at byte
   (tn*(K/128) + tk)*1024, read as 256 little-endian uint32 words. Tile row
@@ -84,6 +90,54 @@ def unpack_ternary(packed: np.ndarray, N: int, K: int, count_invalid: bool = Fal
     m = (packed[byte_p + n_off] >> bit.astype(np.uint8)) & 1
     bad = (p == 1) & (m == 1)
     codes = (p.astype(np.int8) - m.astype(np.int8))
+    codes[bad] = 0
+    if count_invalid:
+        return codes, int(np.count_nonzero(bad))
+    return codes
+
+
+def _mf_byte_and_shift(N: int, K: int):
+    """Byte offset of the 2-bit code of every (n, k) and its shift within that byte,
+    straight from the T2-MF64 text."""
+    n = np.arange(N, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    tn, r = n // 64, n % 64
+    tk, c = k // 64, k % 64
+    f, u = r // 16, r % 16
+    g, j, i = c // 16, (c // 4) % 4, c % 4
+    word = 4 * (16 * g + u) + f
+    wbit = 8 * i + 2 * j
+    byte = (tn * (K // 64) + tk) * 1024 + 4 * word + wbit // 8
+    return byte, np.broadcast_to(wbit % 8, byte.shape)
+
+
+def pack_ternary_mf(codes: np.ndarray, count_invalid: bool = False):
+    """int8 codes [N, K] -> uint8 T2-MF64 bytes [N*K/4]: code w + 1 per weight.
+
+    A code other than -1/0/+1 packs as 0 (code 1) and is counted as invalid.
+    Parity: pinned by hand-worked bytes, the round trip and agreement with T2-PN-64 in
+    the CPU tests."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    assert N % 64 == 0 and K % 64 == 0, "T2-MF64 needs N % 64 == 0 and K % 64 == 0"
+    valid = (codes == 1) | (codes == 0) | (codes == -1)
+    c = np.where(valid, codes.astype(np.int64) + 1, 1)
+    out = np.zeros(ternary_packed_bytes(N, K), dtype=np.uint8)
+    byte, shift = _mf_byte_and_shift(N, K)
+    np.bitwise_or.at(out, byte.ravel(), (c << shift).astype(np.uint8).ravel())
+    if count_invalid:
+        return out, int(np.count_nonzero(~valid))
+    return out
+
+
+def unpack_ternary_mf(packed: np.ndarray, N: int, K: int, count_invalid: bool = False):
+    """T2-MF64 bytes -> int8 codes [N, K]. Code 3 decodes to 0 and is counted invalid."""
+    packed = np.asarray(packed, dtype=np.uint8).ravel()
+    assert packed.size == ternary_packed_bytes(N, K)
+    byte, shift = _mf_byte_and_shift(N, K)
+    c = (packed[byte] >> shift.astype(np.uint8)) & 3
+    bad = c == 3
+    codes = c.astype(np.int8) - 1
     codes[bad] = 0
     if count_invalid:
         return codes, int(np.count_nonzero(bad))

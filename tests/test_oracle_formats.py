@@ -69,6 +69,80 @@ def test_t2_invalid_codes():
     assert bad2 == 1 and codes2[0, 0] == 0
 
 
+# ----------------------------------------------------------------------------- T2-MF64
+# Hand-worked from the layout text on a 128 x 128 matrix whose other codes are -1 (code 0,
+# all bits clear): row r = 16f + u, input c = 16g + 4j + i -> word 4(16g + u) + f, bits
+# 8i + 2j (byte i of the word, shift 2j), value w + 1.
+@pytest.mark.parametrize("n,k,code,byte,value", [
+    (0, 0, 1, 0, 0x02),          # word 0, byte 0, shift 0, code 2
+    (0, 1, 0, 1, 0x01),          # i = 1 -> byte 1, code 1
+    (0, 4, 1, 0, 0x08),          # j = 1 -> shift 2
+    (0, 15, 1, 3, 0x80),         # i = 3, j = 3 -> byte 3, shift 6
+    (0, 16, 0, 256, 0x01),       # g = 1 -> word 64
+    (1, 0, 1, 16, 0x02),         # u = 1 -> word 4
+    (16, 0, 0, 4, 0x01),         # f = 1 -> word 1
+    (63, 63, 1, 1023, 0x80),     # word 255, byte 3, shift 6
+    (0, 64, 1, 1024, 0x02),      # second k tile
+    (64, 0, 0, 2048, 0x01),      # second row band: tile (1, 0)
+    (127, 127, 0, 4095, 0x40),   # tile (1, 1), word 255, byte 3, shift 6, code 1
+])
+def test_mf_worked_bytes(n, k, code, byte, value):
+    codes = np.full((128, 128), -1, dtype=np.int8)
+    codes[n, k] = code
+    packed = oracle.pack_ternary_mf(codes)
+    expect = np.zeros_like(packed)
+    expect[byte] = value
+    assert np.array_equal(packed, expect)
+
+
+def test_mf_layout_is_a_bijection():
+    from oracle.formats import _mf_byte_and_shift
+    byte, shift = _mf_byte_and_shift(128, 192)
+    slots = byte.astype(np.int64) * 8 + shift
+    assert np.unique(slots).size == 128 * 192
+    assert slots.min() == 0 and byte.max() == 128 * 192 // 4 - 1 and np.all(shift % 2 == 0)
+
+
+def test_mf_round_trip_and_agreement_with_t2():
+    codes = synth.ternary_codes(synth.matrix_key(0, 99, 1, 0), 192, 320)
+    mf = oracle.pack_ternary_mf(codes)
+    assert mf.size == oracle.ternary_packed_bytes(192, 320)
+    assert np.array_equal(oracle.unpack_ternary_mf(mf, 192, 320), codes)
+    pn = oracle.pack_ternary(codes)
+    assert np.array_equal(oracle.unpack_ternary(pn, 192, 320), oracle.unpack_ternary_mf(mf, 192, 320))
+    # no word holds the invalid code 3
+    w = _words(mf)
+    for s in range(0, 32, 2):
+        assert not np.any(((w >> s) & 3) == 3)
+
+
+def test_mf_operand_extraction():
+    """The use the layout is cut for: in record 16g + u of a tile, (word f >> 2j) &
+    0x03030303 holds, in byte i, w + 1 of row 16f + u, input 16g + 4j + i."""
+    codes = synth.ternary_codes(synth.matrix_key(0, 99, 2, 0), 64, 64)
+    w = _words(oracle.pack_ternary_mf(codes)).reshape(64, 4)     # [record, f]
+    for g in range(4):
+        for u in range(16):
+            for f in range(4):
+                for j in range(4):
+                    d = (int(w[16 * g + u, f]) >> (2 * j)) & 0x03030303
+                    got = [(d >> (8 * i)) & 0xFF for i in range(4)]
+                    want = [int(codes[16 * f + u, 16 * g + 4 * j + i]) + 1 for i in range(4)]
+                    assert got == want
+
+
+def test_mf_invalid_codes():
+    codes = np.zeros((64, 64), dtype=np.int8)
+    codes[0, :3] = [2, -5, -1]
+    packed, bad = oracle.pack_ternary_mf(codes, count_invalid=True)
+    assert bad == 2
+    assert list(oracle.unpack_ternary_mf(packed, 64, 64)[0, :3]) == [0, 0, -1]
+    packed = packed.copy()
+    packed[0] |= 0x03                                  # code 3 at (0, 0)
+    back, bad2 = oracle.unpack_ternary_mf(packed, 64, 64, count_invalid=True)
+    assert bad2 == 1 and back[0, 0] == 0
+
+
 # ----------------------------------------------------------------------------- S1-128
 @pytest.mark.parametrize("n,k,byte,value", [
     (0, 0, 0, 0x01),        # r = 0, c = 0 -> word 0, bit 0
