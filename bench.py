@@ -157,6 +157,51 @@ def decode_pass(torch, tw, synth, dev, layers, M):
     return items, full_pass, algo_bytes, weight_bytes, launches
 
 
+def repack_stack_mf(torch, tw, dev, layers):
+    """The same 80 layers in T2-MF64, the matrix-core layout of the batched path."""
+    out = []
+    for lg in layers:
+        out.append([(gname, tw.bl_repack_ternary_mf(buf, N, K), N, K) for gname, buf, N, K in lg])
+    torch.cuda.synchronize()
+    return out
+
+
+def decode_pass_mf(torch, tw, synth, dev, layers_mf, M):
+    """Batched decode over T2-MF64 weights: per group one bl_bitlinear_forward_mf call
+    (quantiser + matrix-core product; same activations as decode_pass)."""
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=dev)
+    items = []
+    for li, lg in enumerate(layers_mf):
+        for gi, (gname, buf, N, K) in enumerate(lg):
+            x = torch.from_numpy(synth.normal_fp16((M, K), 0, 5, 1000 + li, gi)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            items.append(dict(x=x, w=buf, N=N, K=K, y=y))
+    ws = tw.workspace(dev, max(tw.bl_workspace_bytes(M, it["N"], it["K"]) for it in items))
+    wsp, wsb = tw.ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    lib, P = tw._lib, tw.ctypes.c_void_p
+    bp = P(beta.data_ptr())
+    args = [(P(it["x"].data_ptr()), it["K"], P(it["w"].data_ptr()), it["N"], P(it["y"].data_ptr()))
+            for it in items]
+
+    def full_pass():
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        for x, K, w, N, y in args:
+            st = lib.bl_bitlinear_forward_mf(x, M, K, w, bp, 1, N, y, wsp, wsb, stream)
+            assert st == 0
+
+    algo_bytes = sum(it["w"].numel() + 2 * M * it["K"] + 4 * M * it["N"] for it in items)
+    weight_bytes = sum(it["w"].numel() for it in items)
+    return items, full_pass, algo_bytes, weight_bytes, 2 * len(items)
+
+
+def bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, steps, warmup):
+    items, full_pass, algo, wbytes, launches = decode_pass_mf(torch, tw, synth, dev, layers_mf, M)
+    run, keep = graphed(torch, full_pass)
+    ms = timed(torch, run, steps, warmup)
+    return dict(ms_per_pass=ms, launches_per_pass=launches, tokens_per_s=M / (ms / 1e3),
+                gbs=algo / (ms / 1e3) / 1e9, weight_gbs=wbytes / (ms / 1e3) / 1e9, graph=True)
+
+
 def graphed(torch, fn):
     """Capture one call of fn into a HIP graph (after a warm-up call) and return its replay."""
     fn()
@@ -472,6 +517,10 @@ def main():
             M = int(args.only.split("_m")[1])
             res = bench_decode70b(torch, tw, synth, dev, layers, M, args.steps, args.warmup,
                                   use_graph=not args.no_graph)
+        elif args.only.startswith("mf_m"):
+            M = int(args.only.split("_m")[1])
+            layers_mf = repack_stack_mf(torch, tw, dev, layers)
+            res = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, args.steps, args.warmup)
         elif args.only.startswith("stack_m"):
             M = int(args.only.split("_m")[1])
             res = bench_decode70b_stack(torch, tw, synth, dev, layers, M, args.steps, args.warmup)
@@ -490,8 +539,15 @@ def main():
         for M in (8, 32, 64):
             r = bench_decode70b(torch, tw, synth, dev, layers, M, max(3, args.steps // 4), 1,
                                 use_graph=not args.no_graph)
-            extra[f"decode70b_m{M}"] = {k: r[k] for k in ("ms_per_pass", "ms_per_pass_eager", "tokens_per_s", "gbs")}
-            log(f"decode70b M={M}:", json.dumps(extra[f'decode70b_m{M}']))
+            extra[f"decode70b_m{M}_t2pn"] = {k: r[k] for k in ("ms_per_pass", "ms_per_pass_eager", "tokens_per_s", "gbs")}
+            log(f"decode70b M={M} (T2-PN-64 weights):", json.dumps(extra[f'decode70b_m{M}_t2pn']))
+        layers_mf = repack_stack_mf(torch, tw, dev, layers)
+        for M in (8, 32, 64):
+            r = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, max(3, args.steps // 4), 1)
+            extra[f"decode70b_m{M}"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs")}
+            extra[f"decode70b_m{M}"]["weights"] = "T2-MF64"
+            log(f"decode70b M={M} (T2-MF64 weights):", json.dumps(extra[f'decode70b_m{M}']))
+        del layers_mf
     del layers
     torch.cuda.empty_cache()
     if not args.skip_extra:

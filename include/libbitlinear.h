@@ -46,6 +46,13 @@
  *  X8-64 (int8 activation bit planes). Row m, 64-input tile t: 16 uint32 words at word
  *    (m*(K/64) + t)*16; word 2b + h holds bit b (two's complement, b = 0..7) of
  *    q[m, 64t + 32h + c] at the same bit positions as T2-PN-64. M*K bytes.
+ *  T2-MF64 (ternary, for the int8 matrix cores). N % 64 == 0, K % 64 == 0. Tiles as
+ *    T2-PN-64 (same order and size), read as 256 uint32 words. Tile row r = 16f + u
+ *    (f = 0..3, u = 0..15) and tile input c = 16g + 4j + i (g, j, i = 0..3) sit in word
+ *    4*(16g + u) + f at bits 8i + 2j .. 8i + 2j + 1, holding the code w + 1 (0, 1, 2;
+ *    3 is invalid). N*K/4 bytes. (Lane 16g + u of a wave loads the 16 bytes at
+ *    16*(16g + u): exactly the weights of its four matrix-core fragments, and
+ *    (word >> 2j) & 0x03030303 is one int8 operand dword of codes.)
  *  S1-128 (sign). N % 64 == 0, K % 128 == 0. Tile (tn, tk) = rows 64tn..+63, inputs
  *    128tk..+127, 1024 bytes at byte (tn*(K/128) + tk)*1024, read as 256 uint32 words.
  *    Tile row r = 16f + u (f = 0..3, u = 0..15) and tile input c = 32s + 8g + 2q + e
@@ -118,6 +125,16 @@ int bl_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* packed,
 int bl_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes,
                       int32_t* n_invalid, void* stream);
 
+/* Pack int8 ternary codes [N, K] into T2-MF64 ([b158] ternary weights at 2 bits each; the
+ * layout serves the int8 matrix-core products below). A code other than -1/0/+1 packs as
+ * 0 and adds 1 to *n_invalid (may be NULL). N % 64 == 0, K % 64 == 0; 16-byte aligned. */
+int bl_pack_ternary_mf(const int8_t* codes, int64_t N, int64_t K, void* packed,
+                       int32_t* n_invalid, void* stream);
+/* Convert T2-PN-64 bytes into T2-MF64 (same weights). A (P, N) = (1, 1) pair becomes 0 and
+ * adds 1 to *n_invalid (may be NULL). The buffers must not overlap. */
+int bl_repack_ternary_mf(const void* t2pn, int64_t N, int64_t K, void* mf, int32_t* n_invalid,
+                         void* stream);
+
 /* Pack the signs of a float weight [N, K] into S1-128 ([onebit] "3. 通过知识蒸馏迁移原模型
  * 能力": Sign(W) is what inference keeps). Bit set iff W < 0, so +0, -0 and NaN give +1.
  * N % 64 == 0, K % 128 == 0; W and packed 16-byte aligned. */
@@ -156,6 +173,27 @@ int bl_bitlinear_gemv(const uint32_t* planes, const float* gamma, int64_t M, int
 int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                       const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
                       float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Batched product from T2-MF64 weights on int8 matrix cores ([b158] "实验及结果": batched
+ * serving; Fig. 3: int8 accumulation), built for batched decode (M <= 64, any M accepted).
+ * The matrix cores multiply q by the codes w + 1; the final sum subtracts rowsum[m], which
+ * must be sum_k q[m,k] (bl_quant_act_int8 computes it), so
+ *   acc[m,n] = sum_k w[n,k] q[m,k]   exactly (int32), and
+ *   y[m,n] = acc[m,n] * (gamma[m] / 127) * beta[beta_len == 1 ? 0 : n].
+ * q int8 [M, K] (16-byte aligned rows), rowsum int32 [M], wmf T2-MF64 [N, K]. Outputs: y fp32
+ * [M, N] (needs gamma and beta) and/or acc int32 [M, N] (either may be NULL, not both).
+ * N % 64 == 0, K % 64 == 0, K <= 65536, M * K < 2^31. Uses ws. */
+int bl_bitlinear_gemm_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                         int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                         int64_t N, float* y, int32_t* acc, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* The whole b1.58 linear from fp16 activations and T2-MF64 weights: quantise (q, gamma and
+ * rowsum into ws), then bl_bitlinear_gemm_mf. Same result as bl_bitlinear_forward on the
+ * same weights in T2-PN-64. x fp16 [M, K]; K <= 28672. Uses ws (bl_workspace_bytes(M, N, K)). */
+int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void* wmf,
+                            const float* beta, int64_t beta_len, int64_t N, float* y, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Debug: the int32 accumulators acc[m,n] = sum_k w[n,k] q[m,k] of the chosen kernel path,
  * before the epilogue. path BL_PATH_GEMV needs planes (M <= 4), BL_PATH_GEMM needs q,

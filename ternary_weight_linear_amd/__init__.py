@@ -58,6 +58,10 @@ _SIGS = {
     "bl_svid_rank1": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
     "bl_residual_binarize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "bl_residual_linear": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "bl_pack_ternary_mf": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "bl_repack_ternary_mf": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "bl_bitlinear_gemm_mf": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bl_bitlinear_forward_mf": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "bl_stack_plan_bytes": (_SZ, [_I64]),
     "bl_stack_prepare": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
     "bl_bitlinear_forward_stack": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
@@ -379,6 +383,61 @@ def bl_residual_linear(x, planes_o, alpha_o, planes_r, alpha_r, out=None):
     _check(_lib.bl_residual_linear(_ptr(x), _ptr(planes_o), _ptr(alpha_o), _ptr(planes_r),
                                    _ptr(alpha_r), M, N, K, _ptr(y), _ptr(ws), wsb, _stream(d)),
            "bl_residual_linear")
+    return y
+
+
+def bl_pack_ternary_mf(codes, n_invalid=None):
+    """int8 codes [N, K] -> T2-MF64 uint8 [N*K/4] (the matrix-core layout)."""
+    _need(codes, torch.int8, "codes")
+    d = _dev(codes)
+    N, K = codes.shape
+    packed = torch.empty(max(_lib.bl_ternary_packed_bytes(N, K), 1), dtype=torch.uint8, device=d)
+    _check(_lib.bl_pack_ternary_mf(_ptr(codes), N, K, _ptr(packed), _ptr(n_invalid), _stream(d)),
+           "bl_pack_ternary_mf")
+    return packed
+
+
+def bl_repack_ternary_mf(t2pn, N: int, K: int, out=None, n_invalid=None):
+    """T2-PN-64 uint8 [N*K/4] -> T2-MF64 uint8 [N*K/4] (same weights)."""
+    _need(t2pn, torch.uint8, "t2pn")
+    d = _dev(t2pn)
+    mf = out if out is not None else torch.empty(max(_lib.bl_ternary_packed_bytes(N, K), 1),
+                                                 dtype=torch.uint8, device=d)
+    _check(_lib.bl_repack_ternary_mf(_ptr(t2pn), N, K, _ptr(mf), _ptr(n_invalid), _stream(d)),
+           "bl_repack_ternary_mf")
+    return mf
+
+
+def bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, beta, N: int, want_y: bool = True,
+                         want_acc: bool = False):
+    """int8 q [M, K], gamma fp32 [M], rowsum int32 [M], T2-MF64 weights -> (y fp32 [M, N] or
+    None, acc int32 [M, N] or None)."""
+    _need(q, torch.int8, "q")
+    _need(rowsum, torch.int32, "rowsum")
+    _need(wmf, torch.uint8, "wmf")
+    d = _dev(q, rowsum, wmf)
+    M, K = q.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=d) if want_y else None
+    acc = torch.empty((M, N), dtype=torch.int32, device=d) if want_acc else None
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_gemm_mf(_ptr(q), _ptr(gamma), _ptr(rowsum), M, K, _ptr(wmf),
+                                     _ptr(beta), _beta_len(beta, N) if beta is not None else 1, N,
+                                     _ptr(y), _ptr(acc), _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_gemm_mf")
+    return y, acc
+
+
+def bl_bitlinear_forward_mf(x, wmf, beta, N: int, out=None):
+    """fp16 x [M, K] -> y fp32 [M, N] from T2-MF64 weights: quantise + matrix-core product."""
+    _half_bits(x, "x")
+    _need(wmf, torch.uint8, "wmf")
+    d = _dev(x, wmf, beta)
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=d)
+    ws, wsb = _ws_for(d, M, N, K)
+    _check(_lib.bl_bitlinear_forward_mf(_ptr(x), M, K, _ptr(wmf), _ptr(beta), _beta_len(beta, N),
+                                        N, _ptr(y), _ptr(ws), wsb, _stream(d)),
+           "bl_bitlinear_forward_mf")
     return y
 
 

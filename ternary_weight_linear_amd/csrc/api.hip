@@ -59,6 +59,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K) {
   take(static_cast<size_t>(M) * K, L.q_off, L.q_bytes);
   take(static_cast<size_t>(M) * K, L.planes_off, L.planes_bytes);
   take(static_cast<size_t>(M) * 4, L.gamma_off, L.gamma_bytes);
+  take(static_cast<size_t>(M) * 4, L.rowsum_off, L.rowsum_bytes);
   take(svid_scratch_floats(N, K) * 4, L.svid_off, L.svid_bytes);
   L.total = off;
   return L;
@@ -178,6 +179,30 @@ int bl_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes, i
                       "bl_unpack_ternary");
 }
 
+int bl_pack_ternary_mf(const int8_t* codes, int64_t N, int64_t K, void* packed,
+                       int32_t* n_invalid, void* stream) {
+  if (!codes || !packed) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 64) return BL_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(packed)) return BL_ERR_ALIGN;
+  if (overlap(codes, N * K, packed, N * K / 4) || overlap(n_invalid, 4, packed, N * K / 4))
+    return BL_ERR_ALIAS;
+  return check_launch(launch_pack_ternary_mf(codes, N, K, packed, n_invalid,
+                                             static_cast<hipStream_t>(stream)),
+                      "bl_pack_ternary_mf");
+}
+
+int bl_repack_ternary_mf(const void* t2pn, int64_t N, int64_t K, void* mf, int32_t* n_invalid,
+                         void* stream) {
+  if (!t2pn || !mf) return BL_ERR_NULL;
+  if (!dims_ok(1, N, K) || N % 64 || K % 64) return BL_ERR_SHAPE;
+  if (!aligned16(t2pn) || !aligned16(mf)) return BL_ERR_ALIGN;
+  if (overlap(t2pn, N * K / 4, mf, N * K / 4) || overlap(n_invalid, 4, mf, N * K / 4))
+    return BL_ERR_ALIAS;
+  return check_launch(launch_repack_pn_to_mf(t2pn, N, K, mf, n_invalid,
+                                             static_cast<hipStream_t>(stream)),
+                      "bl_repack_ternary_mf");
+}
+
 int bl_pack_sign(const float* W, int64_t N, int64_t K, void* packed, void* stream) {
   if (!W || !packed) return BL_ERR_NULL;
   if (!dims_ok(1, N, K) || N % 64 || K % 128) return BL_ERR_SHAPE;
@@ -257,6 +282,66 @@ int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                                   reinterpret_cast<uint32_t*>(w + L.cnt_off),
                                   static_cast<hipStream_t>(stream)),
                       "bl_bitlinear_gemm");
+}
+
+int bl_bitlinear_gemm_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                         int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                         int64_t N, float* y, int32_t* acc, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!q || !rowsum || !wmf || (!y && !acc)) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || K > 65536 || M * K >= (int64_t(1) << 31))
+    return BL_ERR_SHAPE;
+  int st;
+  if (y) {
+    if (!gamma) return BL_ERR_NULL;
+    if ((st = check_beta(beta, beta_len, N))) return st;
+  }
+  if (!aligned16(q) || !aligned16(wmf)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t ob = static_cast<size_t>(M) * N * 4;
+  for (const void* out : {static_cast<const void*>(y), static_cast<const void*>(acc)}) {
+    if (!out) continue;
+    if (overlap(out, ob, q, M * K) || overlap(out, ob, wmf, N * K / 4) ||
+        overlap(out, ob, gamma, gamma ? M * 4 : 0) || overlap(out, ob, rowsum, M * 4) ||
+        overlap(out, ob, beta, y ? beta_len * 4 : 0) || overlap(out, ob, ws, ws_bytes))
+      return BL_ERR_ALIAS;
+  }
+  if (y && acc && overlap(y, ob, acc, ob)) return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  return check_launch(launch_tern_mf(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc,
+                                     reinterpret_cast<uint64_t*>(w + L.acc_off),
+                                     static_cast<hipStream_t>(stream)),
+                      "bl_bitlinear_gemm_mf");
+}
+
+int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void* wmf,
+                            const float* beta, int64_t beta_len, int64_t N, float* y, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!x || !y || !wmf) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || K > 28672 || M * K >= (int64_t(1) << 31))
+    return BL_ERR_SHAPE;
+  int st = check_beta(beta, beta_len, N);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(wmf)) return BL_ERR_ALIGN;
+  const WsLayout L = ws_layout(M, N, K);
+  if (!ws || ws_bytes < L.total) return BL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, wmf, N * K / 4) ||
+      overlap(y, yb, beta, beta_len * 4) || overlap(y, yb, ws, ws_bytes))
+    return BL_ERR_ALIAS;
+  char* w = static_cast<char*>(ws);
+  auto* qbuf = reinterpret_cast<int8_t*>(w + L.q_off);
+  auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
+  auto* rbuf = reinterpret_cast<int32_t*>(w + L.rowsum_off);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_quant_act(x, M, K, qbuf, gbuf, rbuf, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward_mf (quantise)");
+  return check_launch(launch_tern_mf(qbuf, gbuf, rbuf, M, K, wmf, beta, beta_len, N, y, nullptr,
+                                     reinterpret_cast<uint64_t*>(w + L.acc_off), s),
+                      "bl_bitlinear_forward_mf");
 }
 
 int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int64_t K,

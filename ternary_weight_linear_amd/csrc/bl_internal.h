@@ -33,6 +33,7 @@ struct WsLayout {
   size_t q_off, q_bytes;           // int8 [M, K] activations (forward)
   size_t planes_off, planes_bytes; // X8-64 planes [M*K bytes] (forward)
   size_t gamma_off, gamma_bytes;   // fp32 [M] (forward)
+  size_t rowsum_off, rowsum_bytes; // int32 [M] (forward from T2-MF64 weights)
   size_t svid_off, svid_bytes;     // fp32 power-iteration vectors (SVID)
   size_t total;
 };
@@ -50,6 +51,11 @@ hipError_t launch_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* 
                                int32_t* n_invalid, hipStream_t s);
 hipError_t launch_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes,
                                  int32_t* n_invalid, hipStream_t s);
+// T2-MF64 (the matrix-core layout) from codes, or from T2-PN-64 bytes.
+hipError_t launch_pack_ternary_mf(const int8_t* codes, int64_t N, int64_t K, void* packed,
+                                  int32_t* n_invalid, hipStream_t s);
+hipError_t launch_repack_pn_to_mf(const void* pn, int64_t N, int64_t K, void* mf,
+                                  int32_t* n_invalid, hipStream_t s);
 hipError_t launch_pack_sign(const float* W, int64_t N, int64_t K, void* packed, hipStream_t s);
 hipError_t launch_unpack_sign(const void* packed, int64_t N, int64_t K, int8_t* signs,
                               hipStream_t s);
@@ -99,6 +105,11 @@ hipError_t launch_gemv_stack(const void* plan, int64_t count, int64_t M, uint32_
                              uint64_t* ws_acc, hipStream_t s);
 size_t stack_barrier_words();   // zero-maintained uint32 words of the grid-wide wait
 hipError_t stack_read_status(const void* plan, uint32_t* status, hipStream_t s);
+// Ternary GEMM from T2-MF64 weights (int8 matrix cores; rowsum = sum_k q[m, k]); any M,
+// built for M <= 64; M * K < 2^31, K <= 65536.
+hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);
@@ -151,6 +162,38 @@ __device__ __forceinline__ bool split_arrive(uint64_t* word, int32_t partial, in
                                 static_cast<uint32_t>(nsplit) * static_cast<uint32_t>(kSplitOffset));
   __hip_atomic_store(word, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+
+// split_arrive for kN outputs of one lane with one round trip: every add is issued before
+// any returned word is examined (testing each result before the next add would serialise
+// the round trips). word(e) gives element e's split word (called again for the reset, so
+// no pointers stay live); element e takes part iff bit e of `active`, and word(e) must be a
+// valid split word either way (an inactive element adds 0, which changes nothing, so that
+// no add sits behind a branch of its own). The result has bit e set where this lane
+// brought the count to nsplit, v[e] then holding the exact total (and the word cleared).
+template <int kN, class WordFn>
+__device__ __forceinline__ uint32_t split_arrive_batch(WordFn word, int32_t (&v)[kN],
+                                                       uint32_t active, int nsplit) {
+  if (active == 0) return 0;
+  uint64_t now[kN];
+#pragma unroll
+  for (int e = 0; e < kN; ++e) {
+    const uint64_t add = ((active >> e) & 1u)
+                             ? (uint64_t(1) << 32) + static_cast<uint32_t>(v[e] + kSplitOffset)
+                             : uint64_t(0);
+    now[e] = __hip_atomic_fetch_add(word(e), add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+  }
+  uint32_t last = 0;
+#pragma unroll
+  for (int e = 0; e < kN; ++e) {
+    if (((active >> e) & 1u) && (now[e] >> 32) == static_cast<uint64_t>(nsplit)) {
+      v[e] = static_cast<int32_t>(static_cast<uint32_t>(now[e]) -
+                                  static_cast<uint32_t>(nsplit) * static_cast<uint32_t>(kSplitOffset));
+      __hip_atomic_store(word(e), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last |= 1u << e;
+    }
+  }
+  return last;
 }
 
 // Wait until every memory operation this thread issued has completed, and keep the

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // Raw weight rows and activation fragments are fetched S k tiles ahead into registers,
 // weights first (the expansion of tile t + 1 waits for them, and vector loads complete in
 // issue order), and every fetch is unconditional with clamped indices.
-template <int FM, int S>
+template <int FM, int S, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_rb_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ gamma, int64_t M, int64_t K,
     const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
@@ -284,27 +284,55 @@ __global__ __launch_bounds__(256) void gemm_rb_kernel(
     }
   }
 
+  // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r, column l % 16. With K
+  // split, each row tile's 16 outputs of a lane meet the other splits in two batches of 8
+  // adds in flight.
   const int nsplit = gridDim.y;
   const int64_t n0 = static_cast<int64_t>(nt) * 64;
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = m0 + 16 * i + 4 * g + r;
+          const int64_t col = n0 + 16 * j + u;
+          if (row >= M) continue;
+          if (acc_out) acc_out[row * N + col] = acc[i][j][r];
+          if (y) y[row * N + col] = static_cast<float>(acc[i][j][r]) * (gamma[row] / 127.0f) *
+                                    beta[beta_len == 1 ? 0 : col];
+        }
+  } else {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int half = 0; half < 2; ++half) {
+      int32_t v[8];
+      uint32_t active = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r, column l % 16
+      for (int k = 0; k < 8; ++k) {
+        const int j = 2 * half + k / 4, r = k % 4;
+        v[k] = acc[i][j][r];
+        if (m0 + 16 * i + 4 * g + r < M) active |= 1u << k;
+      }
+      auto word = [&](int k) __attribute__((always_inline)) {
+        const int j = 2 * half + k / 4, r = k % 4;
+        return ws_acc + min<int64_t>(m0 + 16 * i + 4 * g + r, M - 1) * N + n0 + 16 * j + u;
+      };
+      const uint32_t done = split_arrive_batch<8>(word, v, active, nsplit);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (!((done >> k) & 1u)) continue;
+        const int j = 2 * half + k / 4, r = k % 4;
         const int64_t row = m0 + 16 * i + 4 * g + r;
         const int64_t col = n0 + 16 * j + u;
-        if (row < M) {
-          int v = acc[i][j][r];
-          if (nsplit > 1 && !split_arrive(&ws_acc[row * N + col], v, nsplit, &v)) continue;
-          if (acc_out) acc_out[row * N + col] = v;
-          if (y) {
-            const float scale = gamma[row] / 127.0f;
-            y[row * N + col] = static_cast<float>(v) * scale * beta[beta_len == 1 ? 0 : col];
-          }
-        }
+        if (acc_out) acc_out[row * N + col] = v[k];
+        if (y) y[row * N + col] = static_cast<float>(v[k]) * (gamma[row] / 127.0f) *
+                                  beta[beta_len == 1 ? 0 : col];
       }
+    }
+  }
 }
 
 // Tuning knobs. Only harnesses that compile this file directly change them; the library
@@ -354,8 +382,16 @@ hipError_t launch_rb(const int8_t* q, const float* gamma, int64_t M, int64_t K, 
   nsplit = std::min(nsplit, kMaxIntSplits);
   const int tps = (KT + nsplit - 1) / nsplit;
   nsplit = (KT + tps - 1) / tps;
-  hipLaunchKernelGGL((gemm_rb_kernel<FM, S>), dim3(static_cast<unsigned>(tiles), nsplit), dim3(256),
-                     0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, tps, MT, NT);
+  // the split hand-off lives in its own instantiation: its registers would otherwise lower
+  // the occupancy of the common unsplit kernel
+  if (nsplit > 1)
+    hipLaunchKernelGGL((gemm_rb_kernel<FM, S, true>), dim3(static_cast<unsigned>(tiles), nsplit),
+                       dim3(256), 0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,
+                       tps, MT, NT);
+  else
+    hipLaunchKernelGGL((gemm_rb_kernel<FM, S, false>), dim3(static_cast<unsigned>(tiles), 1),
+                       dim3(256), 0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,
+                       tps, MT, NT);
   return hipGetLastError();
 }
 

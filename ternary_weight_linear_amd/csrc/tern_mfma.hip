@@ -75,6 +75,48 @@ __device__ __forceinline__ void tern_load(TernTile<FM>& T, const TernArgs& a, in
   for (int fm = 0; fm < FM; ++fm) T.a[fm] = *reinterpret_cast<const u32x4*>(qt + qoff[fm]);
 }
 
+// Epilogue shared by both kernels (wave 0, after the LDS reduction): per 16-row tile fm,
+// the 16 outputs of this lane meet the other K splits with all 16 adds in flight at once
+// (split_arrive_batch; one round trip measured faster here than two batches of 8 with
+// fewer registers), then rowsum (T2-MF64 only) is subtracted and y / acc written.
+// D layout: lane l holds rows 4*(l/16) + i of the q tile, column l % 16 of fragment f.
+template <int FM>
+__device__ __forceinline__ void tern_epilogue(const TernArgs& a, const i32x4 (&acc)[FM][4],
+                                              const int (&red)[3][FM * 16][64], int lane,
+                                              int64_t band, int64_t m0, int nsplit,
+                                              const int32_t* rowsum) {
+  const int g = lane >> 4, u = lane & 15;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    // output k = 4 f + i: row m0 + 16 fm + 4g + i, column band * 64 + 16 f + u
+    int32_t v[16];
+    uint32_t active = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int f = k / 4, i = k % 4, e = (fm * 4 + f) * 4 + i;
+      v[k] = acc[fm][f][i] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+      if (m0 + 16 * fm + 4 * g + i < a.M) active |= 1u << k;
+    }
+    auto word = [&](int k) __attribute__((always_inline)) {
+      const int64_t row = min<int64_t>(m0 + 16 * fm + 4 * g + k % 4, a.M - 1);
+      return a.ws_acc + row * a.N + band * 64 + 16 * (k / 4) + u;
+    };
+    const uint32_t done = nsplit > 1 ? split_arrive_batch<16>(word, v, active, nsplit) : active;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (!((done >> k) & 1u)) continue;
+      const int64_t row = m0 + 16 * fm + 4 * g + k % 4;
+      const int64_t col = band * 64 + 16 * (k / 4) + u;
+      int r = v[k];
+      if (rowsum) r -= rowsum[row];
+      if (a.acc_out) a.acc_out[row * a.N + col] = r;
+      if (a.y)
+        a.y[row * a.N + col] = static_cast<float>(r) * (a.gamma[row] / 127.0f) *
+                               a.beta[a.beta_len == 1 ? 0 : col];
+    }
+  }
+}
+
 // SPLIT: multiply the +1 flags and the -1 flags separately (two MFMAs, acc = accP - accN,
 // four VALU ops per 16 weights); otherwise expand to int8 first (one MFMA, six VALU ops).
 // The first suits few rows of q (VALU-bound), the second many (matrix-core-bound).
@@ -180,24 +222,112 @@ __global__ __launch_bounds__(256) void tern_mfma_kernel(const TernArgs a) {
   }
   __syncthreads();
   if (wave > 0) return;
+  tern_epilogue<FM>(a, acc, red, lane, band, m0, nsplit, nullptr);
+}
+
+// ---- T2-MF64 weights -------------------------------------------------------------------
+// The second ternary layout stores, for each lane 16g + u of a wave, the 16 bytes its four
+// fragments need: word f holds codes w + 1 of weight row 16f + u, inputs 16g + 4j + i at
+// bits 8i + 2j. So a tile costs one 16-byte load per lane (no lane loads bytes another
+// lane also loads), (word >> 2j) & 0x03030303 is one operand dword (seven ALU ops per
+// fragment) and one MFMA per fragment multiplies q by w + 1. The final writer subtracts
+// sum_k q[m, k] (from the quantiser), which makes the integers those of q . w exactly.
+// A split's partial |sum q (w + 1)| <= 254 * 64 * tiles stays below the split words' 2^23
+// bias as long as a split spans at most kMfMaxSplitTiles tiles.
+#ifndef BL_MF_DEPTH
+#define BL_MF_DEPTH 3
+#endif
+constexpr int kMfDepth = BL_MF_DEPTH;
+constexpr int kMfMaxSplitTiles = ((1 << 23) - 1) / (254 * 64);   // 516
+
+template <int FM>
+struct MfTile {
+  u32x4 w;               // record 16g + u of the tile: words f = 0..3
+  u32x4 a[FM];           // q[m0 + 16fm + u, 64t + 16g .. +15]
+};
+
+template <int FM>
+__device__ __forceinline__ void mf_load(MfTile<FM>& T, const TernArgs& a, int64_t band,
+                                        const uint32_t (&qoff)[FM], int lane, int t, int KT) {
+  T.w = a.W[(band * KT + t) * 64 + lane];
+  const char* qt = reinterpret_cast<const char*>(a.q) + static_cast<int64_t>(t) * 64;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) T.a[fm] = *reinterpret_cast<const u32x4*>(qt + qoff[fm]);
+}
+
+template <int FM>
+__device__ __forceinline__ void mf_compute(const MfTile<FM>& T, i32x4 (&acc)[FM][4]) {
+  const uint32_t w4[4] = {T.w.x, T.w.y, T.w.z, T.w.w};
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    i32x4 b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = static_cast<int>((w4[f] >> (2 * j)) & 0x03030303u);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      acc[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, T.a[fm]), b,
+                                                         acc[fm][f], 0, 0, 0);
+  }
+}
+
+// Same mapping as tern_mfma_kernel: a workgroup owns one 64-column band, FM 16-row tiles of
+// q and a K range whose tiles its four waves take in turn (kMfDepth - 1 in flight, loads
+// clamped and unconditional), meeting in LDS with exact int32 sums.
+template <int FM>
+__global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
+                                                      const int32_t* __restrict__ rowsum) {
+  constexpr int P = kMfDepth;
+  constexpr int kRows = 16 * FM;
+  __shared__ int red[3][FM * 16][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, u = lane & 15;
+  const int64_t band = blockIdx.x;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRows;
+  const int split = blockIdx.z, nsplit = gridDim.z;
+  const int KT = static_cast<int>(a.K / 64);
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(KT, t0 + a.tiles_per_split);
+  uint32_t qoff[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t row = min<int64_t>(m0 + 16 * fm + u, a.M - 1);
+    qoff[fm] = static_cast<uint32_t>(row * a.K + 16 * g);   // M*K < 2^31 (checked on the host)
+  }
+  i32x4 acc[FM][4];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < 4; ++f) acc[fm][f] = i32x4{0, 0, 0, 0};
+
+  const int first = t0 + wave;
+  const int n = first < t1 ? (t1 - first + 3) / 4 : 0;
+  const int last = n > 0 ? first + 4 * (n - 1) : t1 - 1;
+  MfTile<FM> T[P];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = (fm * 4 + f) * 4 + i;
-        int v = acc[fm][f][i] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
-        // D layout: lane l holds rows 4*(l/16) + i of the q tile, column l % 16 of fragment f
-        const int64_t row = m0 + 16 * fm + 4 * g + i;
-        const int64_t col = band * 64 + 16 * f + u;
-        if (row >= a.M) continue;
-        if (nsplit > 1 && !split_arrive(&a.ws_acc[row * a.N + col], v, nsplit, &v)) continue;
-        if (a.acc_out) a.acc_out[row * a.N + col] = v;
-        if (a.y)
-          a.y[row * a.N + col] = static_cast<float>(v) * (a.gamma[row] / 127.0f) *
-                                 a.beta[a.beta_len == 1 ? 0 : col];
-      }
+  for (int d = 0; d < P - 1; ++d) mf_load<FM>(T[d], a, band, qoff, lane, min(first + 4 * d, last), KT);
+  for (int j0 = 0; j0 < n; j0 += P) {
+#pragma unroll
+    for (int d = 0; d < P; ++d) {
+      const int j = j0 + d;
+      mf_load<FM>(T[(d + P - 1) % P], a, band, qoff, lane, min(first + 4 * (j + P - 1), last), KT);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < n) mf_compute<FM>(T[d], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  if (wave > 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][(fm * 4 + f) * 4 + i][lane] = acc[fm][f][i];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  tern_epilogue<FM>(a, acc, red, lane, band, m0, nsplit, rowsum);
 }
 
 struct TernPlan { int64_t bands, mgroups, nsplit, tps; int fm; bool split; };
@@ -231,6 +361,34 @@ TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
 }
 
 }  // namespace
+
+// Workgroups the T2-MF64 kernel aims for (0: 512); tuning harnesses only.
+int64_t g_mf_wg_target = 0;
+
+hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
+  // measured on MI355X (70B-shaped decode, M = 8..64): one 16-row tile of q per wave and
+  // many workgroups beat wider tiles that read each weight once (the extra weight reads
+  // cost less than the lost parallelism); K is split until ~512 workgroups
+  const int64_t KT = K / 64, bands = N / 64;
+  const int64_t mgroups = (M + 15) / 16;
+  const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 512;
+  int64_t nsplit = (target + bands * mgroups - 1) / (bands * mgroups);
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
+  nsplit = std::max<int64_t>(nsplit, (KT + kMfMaxSplitTiles - 1) / kMfMaxSplitTiles);
+  if (M * N > kAccCap) nsplit = 1;
+  nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
+  int64_t tps = (KT + nsplit - 1) / nsplit;
+  nsplit = (KT + tps - 1) / tps;
+  if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
+  TernArgs a{q, gamma, static_cast<const u32x4*>(wmf), beta, beta_len, M, N, K, y, acc_out,
+             ws_acc, static_cast<int>(tps)};
+  const dim3 grid(static_cast<unsigned>(bands), static_cast<unsigned>(mgroups),
+                  static_cast<unsigned>(nsplit));
+  hipLaunchKernelGGL((tern_mf_kernel<1>), grid, dim3(256), 0, s, a, rowsum);
+  return hipGetLastError();
+}
 
 hipError_t launch_tern_mfma(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                             const void* wpacked, const float* beta, int64_t beta_len, int64_t N,

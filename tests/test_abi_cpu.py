@@ -197,3 +197,48 @@ def test_stack_checks(lib):
     assert lib.bl_bitlinear_forward_stack(_p(plan), 2, M, _p(A), 4096, None) == WS
     assert lib.bl_bitlinear_forward_stack(_p(plan), 2, M, _p(A + 16), wsb, None) == ALIGN
     assert lib.bl_stack_status(None, None) < 0
+
+
+def test_mf_checks(lib):
+    N, K, M = 128, 256, 8
+    pb = N * K // 4
+    # packers
+    assert lib.bl_pack_ternary_mf(None, N, K, _p(B), None, None) == NULL
+    assert lib.bl_pack_ternary_mf(_p(A), 100, K, _p(B), None, None) == SHAPE
+    assert lib.bl_pack_ternary_mf(_p(A), N, 96, _p(B), None, None) == SHAPE
+    assert lib.bl_pack_ternary_mf(_p(A + 4), N, K, _p(B), None, None) == ALIGN
+    assert lib.bl_pack_ternary_mf(_p(A), N, K, _p(A + 64), None, None) == ALIAS
+    assert lib.bl_repack_ternary_mf(_p(A), N, K, None, None, None) == NULL
+    assert lib.bl_repack_ternary_mf(_p(A), N, K, _p(A + 256), None, None) == ALIAS
+    assert lib.bl_repack_ternary_mf(_p(A), N, K, _p(B + 8), None, None) == ALIGN
+    wsb = lib.bl_workspace_bytes(M, N, K)
+
+    def gemm(**kw):
+        a = dict(q=_p(A), g=_p(A + 0x10000), r=_p(A + 0x20000), M=M, K=K, w=_p(B), b=_p(A + 0x30000),
+                 bl=1, N=N, y=_p(C), acc=None, ws=_p(D), wsb=wsb)
+        a.update(kw)
+        return lib.bl_bitlinear_gemm_mf(a["q"], a["g"], a["r"], a["M"], a["K"], a["w"], a["b"], a["bl"],
+                                         a["N"], a["y"], a["acc"], a["ws"], a["wsb"], None)
+    assert gemm(r=None) == NULL
+    assert gemm(y=None, acc=None) == NULL
+    assert gemm(g=None) == NULL
+    assert gemm(N=96) == SHAPE
+    assert gemm(K=65536 + 64) == SHAPE
+    assert gemm(M=1 << 16, K=1 << 15) == SHAPE            # M * K >= 2^31
+    assert gemm(bl=3) == ARG
+    assert gemm(q=_p(A + 8)) == ALIGN
+    assert gemm(wsb=1024) == WS
+    assert gemm(y=_p(B + 64)) == ALIAS                    # output over the weights
+    assert gemm(y=None, acc=_p(A + 0x20000)) == ALIAS     # acc over rowsum
+    assert gemm(acc=_p(C + 16)) == ALIAS                  # y and acc overlap
+
+    def fwd(**kw):
+        a = dict(x=_p(A), M=M, K=K, w=_p(B), b=_p(C), bl=1, N=N, y=_p(D + 0x10000000), ws=_p(D), wsb=wsb)
+        a.update(kw)
+        return lib.bl_bitlinear_forward_mf(a["x"], a["M"], a["K"], a["w"], a["b"], a["bl"], a["N"],
+                                           a["y"], a["ws"], a["wsb"], None)
+    assert fwd(x=None) == NULL
+    assert fwd(K=28672 + 64) == SHAPE
+    assert fwd(x=_p(A + 2)) == ALIGN
+    assert fwd(wsb=100) == WS
+    assert fwd(y=_p(A + 16)) == ALIAS

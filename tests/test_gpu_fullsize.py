@@ -133,3 +133,18 @@ def test_stack_kernel_full_size(layer0, M):
         if i < 4:
             ids, yref = _sampled_reference(x16, parts, K, 16, seed=100 + i + 10 * M)
             assert_rel(host(y)[:, ids], yref)
+
+
+@pytest.mark.parametrize("M", [8, 64])
+def test_mf_layer_sampled_rows(layer0, M):
+    """The 70B layer repacked into T2-MF64 (the benchmark's batched-decode configuration):
+    quantiser + matrix-core product, sampled rows against the oracle."""
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
+    for gi, (gname, buf, N, K, parts) in enumerate(layer0):
+        say("fullsize mf", gname, "M", M)
+        wmf = tw.bl_repack_ternary_mf(buf, N, K)
+        x16 = synth.normal_fp16((M, K), 0, 5, 4000, gi)
+        y = tw.bl_bitlinear_forward_mf(torch.from_numpy(x16).to(DEV), wmf, beta, N)
+        ids, yref = _sampled_reference(x16, parts, K, 32, seed=200 + gi + 10 * M)
+        assert_rel(host(y)[:, ids], yref)
+        del wmf

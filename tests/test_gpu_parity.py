@@ -568,3 +568,78 @@ def test_stack_leaves_workspace_zero():
     zero_prefix = 65536 * 4 + 64 * 65536 * 8        # counters (incl. the arrival counter) + split words
     for d, buf in tw._ws.items():
         assert not host(buf[:zero_prefix]).any(), "zero-maintained workspace left dirty"
+
+
+# ----------------------------------------------------------------------------- T2-MF64
+@pytest.mark.parametrize("N,K", [(64, 64), (192, 320), (1024, 3200)])
+def test_pack_and_repack_ternary_mf(N, K):
+    say("pack mf", N, K)
+    codes = synth.ternary_codes(synth.matrix_key(0, 130, N, K), N, K)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mf = tw.bl_pack_ternary_mf(dev(codes), n_invalid=bad)
+    assert np.array_equal(host(mf), oracle.pack_ternary_mf(codes)) and int(host(bad)[0]) == 0
+    mf2 = tw.bl_repack_ternary_mf(tw.bl_pack_ternary(dev(codes)), N, K, n_invalid=bad)
+    assert np.array_equal(host(mf2), oracle.pack_ternary_mf(codes)) and int(host(bad)[0]) == 0
+
+
+def test_mf_invalid_codes():
+    say("mf invalid")
+    codes = np.zeros((64, 64), dtype=np.int8)
+    codes[0, :3] = [2, -5, -1]
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mf = tw.bl_pack_ternary_mf(dev(codes), n_invalid=bad)
+    assert int(host(bad)[0]) == 2
+    assert np.array_equal(host(mf), oracle.pack_ternary_mf(codes))
+    pn = oracle.pack_ternary(np.zeros((64, 64), dtype=np.int8))
+    pn[0] |= 0x01                                   # P and N both set at (0, 0)
+    pn[8] |= 0x01
+    bad.zero_()
+    mf2 = tw.bl_repack_ternary_mf(dev(pn), 64, 64, n_invalid=bad)
+    assert int(host(bad)[0]) == 1
+    assert np.array_equal(host(mf2), oracle.pack_ternary_mf(np.zeros((64, 64), dtype=np.int8)))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 192, 320), (8, 512, 512), (16, 640, 1024),
+                                   (17, 384, 448), (33, 256, 640), (64, 1024, 8192),
+                                   (100, 256, 640), (2, 128, 39936), (8, 8192, 28672)])
+def test_gemm_mf_acc_and_output(M, N, K):
+    say("gemm mf", M, N, K)
+    codes = synth.ternary_codes(synth.matrix_key(0, 131, N, K), N, K)
+    if K <= 28672:
+        x = synth.normal_fp16((M, K), 0, 132, M, K)
+        q, gamma, rowsum, _ = tw.bl_quant_act_int8(dev(x), want_planes=False)
+        rq, rg, rrow = oracle.quant_act_int8(x)
+        assert np.array_equal(host(rowsum), rrow)
+    else:
+        # rows longer than the quantiser takes: int8 activations drawn directly (the
+        # extremes included), with gamma = 127 and their row sums as the kernel's inputs
+        rq = synth.rng(0, 135, M, K).integers(-127, 128, size=(M, K)).astype(np.int8)
+        rq[:, :2] = [127, -127]
+        rg = np.full(M, 127.0, dtype=np.float32)
+        q, gamma = dev(rq), dev(rg)
+        rowsum = dev(rq.astype(np.int64).sum(axis=1).astype(np.int32))
+    wmf = tw.bl_pack_ternary_mf(dev(codes))
+    beta = np.float32(synth.BETA_DIRECT)
+    y, acc = tw.bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, dev(np.array([beta])), N, want_acc=True)
+    ref_acc = oracle.acc_exact(rq, codes)
+    assert np.array_equal(host(acc), ref_acc)
+    assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, beta))
+    y2, _ = tw.bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, dev(np.array([beta])), N)
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 512, 512), (32, 320, 1024), (64, 1024, 8192)])
+def test_forward_mf_equals_forward(M, N, K):
+    """The same weights as T2-MF64 and T2-PN-64 give identical outputs (both kernels sum the
+    exact integers and apply one epilogue)."""
+    say("forward mf", M, N, K)
+    x = synth.normal_fp16((M, K), 0, 133, M, K)
+    W = synth.normal_fp32((N, K), 0, 134, N, K, std=0.02)
+    packed, beta, _ = tw.bl_ternarize_absmean(dev(W))
+    wmf = tw.bl_repack_ternary_mf(packed, N, K)
+    y_pn = tw.bl_bitlinear_forward(dev(x), packed, beta, N, path=tw.BL_PATH_GEMM)
+    y_mf = tw.bl_bitlinear_forward_mf(dev(x), wmf, beta, N)
+    assert np.array_equal(host(y_pn).view(np.uint32), host(y_mf).view(np.uint32))
+    codes, rbeta = oracle.ternarize_absmean(W)
+    yref, _, _, _ = oracle.bitlinear_forward(x, codes, rbeta)
+    assert_rel(host(y_mf), yref)
