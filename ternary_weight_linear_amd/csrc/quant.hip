@@ -8,7 +8,8 @@
 // One workgroup per token row. Pass 1 copies the fp16 row into LDS while reducing |x| to
 // gamma with wavefront reductions. Pass 2 gives each wave one 64-input tile at a time:
 // lane l holds the input whose X8-64 bit position is l, so eight __ballot calls produce
-// the eight activation bit planes of the tile directly.
+// the eight activation bit planes of the tile directly. When no planes are asked for, a
+// second kernel keeps the row in registers instead (below).
 #include "bl_internal.h"
 
 namespace bl {
@@ -101,10 +102,103 @@ __global__ __launch_bounds__(BLOCK) void quant_act_kernel(const uint16_t* __rest
   }
 }
 
+// Without bit planes the lane order of pass 2 is not needed: each thread quantises the
+// (up to NV x 8) inputs it loaded, straight from registers, and stores them as contiguous
+// bytes. Same arithmetic per element; one load, two workgroup barriers (gamma, row sum).
+template <int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t K, int8_t* __restrict__ q,
+                                                               float* __restrict__ gamma,
+                                                               int32_t* __restrict__ rowsum) {
+  __shared__ float red_max[BLOCK / 64];
+  __shared__ int red_bad[BLOCK / 64];
+  __shared__ int red_sum[BLOCK / 64];
+  constexpr int NW = BLOCK / 64;
+  const int64_t m = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint4* row4 = reinterpret_cast<const uint4*>(x + m * K);
+  const int64_t K8 = K / 8;
+  uint4 v[NV];
+#pragma unroll
+  for (int n = 0; n < NV; ++n) v[n] = row4[min<int64_t>(threadIdx.x + BLOCK * n, K8 - 1)];
+  float mx = 0.0f;
+  int bad = 0;
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const uint32_t w[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t lo = static_cast<uint16_t>(w[j] & 0xFFFFu), hi = static_cast<uint16_t>(w[j] >> 16);
+      bad |= ((lo & 0x7C00u) == 0x7C00u) | ((hi & 0x7C00u) == 0x7C00u);
+      mx = fmaxf(mx, fabsf(half_bits_to_float(lo)));
+      mx = fmaxf(mx, fabsf(half_bits_to_float(hi)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    bad |= __shfl_xor(bad, off);
+  }
+  if (lane == 0) { red_max[wave] = mx; red_bad[wave] = bad; }
+  __syncthreads();
+  mx = red_max[0];
+  bad = red_bad[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, red_max[w]); bad |= red_bad[w]; }
+  const float g = bad ? __uint_as_float(0x7FC00000u) : mx;
+  if (threadIdx.x == 0) gamma[m] = g;
+  const bool zero = bad || mx == 0.0f;
+
+  int sum = 0;
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int64_t i = threadIdx.x + BLOCK * n;
+    if (i >= K8) break;
+    const uint32_t w[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t hb = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      int qv = 0;
+      if (!zero) {
+        const float r = rintf(half_bits_to_float(hb) * 127.0f / g);   // exact product, IEEE division
+        qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
+      }
+      sum += qv;
+      packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * (e & 3));
+    }
+    if (q) *reinterpret_cast<uint2*>(q + m * K + 8 * i) = make_uint2(packed[0], packed[1]);
+  }
+  if (rowsum) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) red_sum[wave] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int s = 0;
+      for (int w = 0; w < NW; ++w) s += red_sum[w];
+      rowsum[m] = s;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* gamma,
                             int32_t* rowsum, uint32_t* planes, hipStream_t s) {
+  if (!planes) {
+    // one workgroup per row, every input of the row in registers
+    const int64_t K8 = K / 8;
+    if (M <= 64) {
+      if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<1024, 1>), dim3(static_cast<unsigned>(M)), dim3(1024), 0, s, x, K, q, gamma, rowsum);
+      else hipLaunchKernelGGL((quant_act_regs_kernel<1024, 4>), dim3(static_cast<unsigned>(M)), dim3(1024), 0, s, x, K, q, gamma, rowsum);
+    } else {
+      if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<256, 4>), dim3(static_cast<unsigned>(M)), dim3(256), 0, s, x, K, q, gamma, rowsum);
+      else hipLaunchKernelGGL((quant_act_regs_kernel<256, 16>), dim3(static_cast<unsigned>(M)), dim3(256), 0, s, x, K, q, gamma, rowsum);
+    }
+    return hipGetLastError();
+  }
   const size_t lds = static_cast<size_t>(K) * sizeof(uint16_t);
   if (M <= 64) {
     hipLaunchKernelGGL(quant_act_kernel<1024>, dim3(static_cast<unsigned>(M)), dim3(1024), lds, s,

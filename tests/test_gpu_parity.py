@@ -97,18 +97,24 @@ def test_ternarize_absmean_edge_cases():
 
 # ----------------------------------------------------------------------------- quantiser
 def _quant_case(x):
+    """Both kernels: with bit planes (LDS row, lane order of the planes) and without (the
+    row kept in registers); q, gamma and row sums identical to the oracle either way."""
     M, K = x.shape
-    q, gamma, rowsum, planes = tw.bl_quant_act_int8(dev(x))
     rq, rg, rr = oracle.quant_act_int8(x)
-    gg = host(gamma)
-    assert np.array_equal(np.isnan(gg), np.isnan(rg))
-    assert np.array_equal(gg[~np.isnan(rg)].view(np.uint32), rg[~np.isnan(rg)].view(np.uint32))
-    assert np.array_equal(host(q), rq)
-    assert np.array_equal(host(rowsum), rr)
-    assert np.array_equal(host(planes).view(np.uint32).reshape(M, K // 64, 16), oracle.act_planes(rq))
+    for want_planes in (True, False):
+        q, gamma, rowsum, planes = tw.bl_quant_act_int8(dev(x), want_planes=want_planes)
+        gg = host(gamma)
+        assert np.array_equal(np.isnan(gg), np.isnan(rg))
+        assert np.array_equal(gg[~np.isnan(rg)].view(np.uint32), rg[~np.isnan(rg)].view(np.uint32))
+        assert np.array_equal(host(q), rq)
+        assert np.array_equal(host(rowsum), rr)
+        if want_planes:
+            assert np.array_equal(host(planes).view(np.uint32).reshape(M, K // 64, 16),
+                                  oracle.act_planes(rq))
 
 
-@pytest.mark.parametrize("M,K", [(1, 64), (8, 512), (3, 640), (1, 8192), (4, 28672), (512, 3200)])
+@pytest.mark.parametrize("M,K", [(1, 64), (8, 512), (3, 640), (1, 8192), (4, 28672), (512, 3200),
+                                 (65, 8192), (70, 28672), (64, 8256)])
 def test_quant_act(M, K):
     say("quant_act", M, K)
     x = synth.normal_fp16((M, K), 0, 2, M, K)
