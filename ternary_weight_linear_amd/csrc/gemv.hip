@@ -21,6 +21,8 @@
 // restores the workspace to zero.
 #include "bl_internal.h"
 
+#include <type_traits>
+
 namespace bl {
 namespace {
 
@@ -115,9 +117,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // inside the kernel instead of read from X8-64 memory. A workgroup owns kFW consecutive
 // 64-row bands (one per wave) and one K range, processed in chunks of up to kChunk tiles:
 //  1. loads are issued at once: first this thread's share of the row for gamma and the x
-//     values its wave quantises in the first chunk, then the wave's first kRing - 1 weight
-//     batches, so HBM streaming starts before anything else (vector loads complete in
-//     issue order, so the x-dependent steps never wait for weights);
+//     values its wave quantises in the first chunk, then the wave's first weight batch, so
+//     HBM streaming runs through steps 2-3 (vector loads complete in issue order, so the
+//     x-dependent steps never wait for weights); the ring's other batches follow between
+//     the tiles of step 3;
 //  2. gamma: every workgroup reduces |x| over the whole row. For finite fp16 the magnitude
 //     order equals the integer order of the bits with the sign cleared, so this is an
 //     integer max over masked bit patterns (no conversions); a maximum >= 0x7C00 flags
@@ -125,14 +128,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 //  3. each wave quantises every kFW-th tile of the chunk (lane l takes the input whose plane
 //     bit is l; eight wave ballots give the tile's planes) into LDS, then one barrier;
 //  4. each wave runs the select + popcount loop over the chunk for its own band with a ring
-//     of kRing register batches, kRing - 1 of them in flight, planes read from LDS as
-//     wave-uniform broadcasts.
+//     of kRing register batches, each slot refilled with the batch kRing ahead as soon as
+//     it is reduced, planes read from LDS as wave-uniform broadcasts.
+// Weights are read through a buffer resource that spans the wave's band over the
+// workgroup's K range: loads past the range return zero without a memory access, so the
+// stream is issued ahead unconditionally (no clamped re-reads at the end of a range).
 // The integer results are identical to bl_quant_act_int8 followed by the GEMV.
 #ifndef BL_GEMVF_BATCH
-#define BL_GEMVF_BATCH 8
+#define BL_GEMVF_BATCH 4
 #endif
 #ifndef BL_GEMVF_RING
-#define BL_GEMVF_RING 2
+#define BL_GEMVF_RING 4
 #endif
 constexpr int kBatch = BL_GEMVF_BATCH;      // tiles per register batch
 constexpr int kRing = BL_GEMVF_RING;        // register batches per wave
@@ -143,6 +149,25 @@ constexpr int kChunk = 64;                  // tiles whose planes sit in LDS at 
 constexpr int kFW = BL_GEMVF_WAVES;         // waves (bands) per workgroup
 
 constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chunk
+static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit elements
+
+// q = rint(a / g) for a = x * 127 (exact in fp32) and |a| <= 127 g, decided on the correctly
+// rounded fp32 quotient. d = a * rcp(g) is within 3.1e-5 of that quotient (rcp 1 ulp, product
+// 0.5 ulp, |a / g| <= 127), so the two round to the same integer unless a half-integer lies
+// within that distance of d; such inputs (fractional part within 2^-12 of 1/2) take the IEEE
+// division instead (behind a wave-uniform test, so that the common case skips it).
+__device__ __forceinline__ int quant_q(float a, float g, float rg) {
+  float d = a * rg;
+  const bool near = fabsf(__builtin_amdgcn_fractf(d) - 0.5f) < 0x1p-12f;
+  if (__ballot(near) != 0) {
+    float gv = g;
+    asm volatile("" : "+v"(gv));   // keeps the division inside the branch (no speculation)
+    const float e = a / gv;
+    d = near ? e : d;
+  }
+  return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d), -127.0f, 127.0f));
+}
 
 template <int MR, int GL>
 __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
@@ -161,17 +186,24 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
   const int KT = static_cast<int>(K / 64);
   const int t0 = split * tiles_per_split;
   const int t1 = min(KT, t0 + tiles_per_split);
-  const u32x4* wp = W + (active ? band : 0) * KT * 64 + lane;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(W + ((active ? band : 0) * KT + t0) * 64), 0,
+      active && t1 > t0 ? (t1 - t0) * 1024 : 0, kRsrcWord3);
   // lane l <-> plane bit l of a tile: half h = l / 32, bit p = l % 32 = 8i + j <-> c = 4j + i
   const int koff = 32 * (lane >> 5) + 4 * (lane & 7) + ((lane & 31) >> 3);
 
-  // All loads below are unconditional (indices past the range are clamped to its last
-  // tile, and such values are never used): branch-free code lets the compiler wait for
-  // exactly the loads a step needs instead of for every load in flight.
+  // All loads below are unconditional (x indices past the range are clamped, weight tiles
+  // past it read as zero): branch-free code lets the compiler wait for exactly the loads a
+  // step needs instead of for every load in flight.
   u32x4 w[kRing][kBatch];
-  auto load_batch = [&](u32x4 (&dst)[kBatch], int tb, int tend) {
+  auto load_batch = [&](u32x4 (&dst)[kBatch], int rel) {   // tiles t0 + rel .. + kBatch - 1
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) dst[u] = wp[static_cast<int64_t>(min(tb + u, tend - 1)) * 64];
+    for (int u = 0; u < kBatch; ++u)
+      dst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wr, (rel + u) * 1024 + lane * 16, 0, 0));
+    // keep each batch where it is issued: the scheduler would otherwise interleave or sink
+    // batches, and the waits for one batch would then cover the next as well
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto load_x = [&](uint16_t (&xq)[kPerWave][MR], int c0, int c1) {
 #pragma unroll
@@ -196,14 +228,13 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
   }
   uint16_t xq[kPerWave][MR];
   load_x(xq, t0, min(t1, t0 + kChunk));
-  {
-    const int c1 = min(t1, t0 + kChunk);
-#pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) load_batch(w[r], t0 + r * kBatch, c1);
-  }
+  load_batch(w[0], 0);   // the rest of the ring is issued between the quantised tiles: a wave
+                         // issues its loads in order, and the vector memory path takes
+                         // ~16 cycles per 1 KiB load, so issuing them here would hold the
+                         // gamma fold back
 
   // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
-  float g[MR];
+  float g[MR], rg[MR];
   bool zero[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -233,6 +264,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
     const bool bad = mb >= 0x7C00u;
     g[m] = bad ? __uint_as_float(0x7FC00000u) : half_bits_to_float(static_cast<uint16_t>(mb));
     zero[m] = bad || mb == 0u;
+    rg[m] = __builtin_amdgcn_rcpf(zero[m] ? 1.0f : g[m]);
   }
 
   int A[MR][8];
@@ -242,26 +274,19 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
     for (int b = 0; b < 8; ++b) A[m][b] = 0;
   int cn = 0;
 
-  for (int c0 = t0; c0 < t1; c0 += kChunk) {
-    const int c1 = min(t1, c0 + kChunk);
-    if (c0 != t0) {
-      __syncthreads();                    // the previous chunk's planes are consumed
-      load_x(xq, c0, c1);                 // before the weights: see above
-#pragma unroll
-      for (int r = 0; r < kRing - 1; ++r) load_batch(w[r], c0 + r * kBatch, c1);
-    }
-    // quantise tiles c0 + wave + 4j of this chunk into LDS
+  // quantise tiles c0 + wave + kFW j of a chunk into LDS; in the first chunk, the ring's
+  // remaining batches are issued between the tiles
+  auto quantise = [&](int c0, int c1, auto first) {
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
+      if constexpr (decltype(first)::value) {
+        if (j + 1 < kRing) load_batch(w[j + 1], (j + 1) * kBatch);
+      }
       const int tt = c0 + wave + kFW * j;
       if (tt < c1) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          int qv = 0;
-          if (!zero[m]) {
-            const float r = rintf(half_bits_to_float(xq[j][m]) * 127.0f / g[m]);
-            qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
-          }
+          const int qv = zero[m] ? 0 : quant_q(half_bits_to_float(xq[j][m]) * 127.0f, g[m], rg[m]);
           uint32_t mine = 0;
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
@@ -272,23 +297,37 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
         }
       }
     }
+  };
+  static_assert(kRing - 1 <= kPerWave, "the ring is issued within the first chunk");
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const int c1 = min(t1, c0 + kChunk);
+    if (c0 == t0) {
+      quantise(c0, c1, std::true_type{});
+    } else {
+      __syncthreads();                    // the previous chunk's planes are consumed
+      load_x(xq, c0, c1);                 // (this chunk's first batches are already in flight)
+      quantise(c0, c1, std::false_type{});
+    }
     __syncthreads();
     if (active) {
-      // batch i of the chunk sits in ring slot i % kRing; batch i + kRing - 1 is issued
-      // (clamped, so unconditionally) before batch i is reduced
+      // batch i of the range sits in ring slot i % kRing; once reduced, the slot is refilled
+      // with batch i + kRing (unconditionally: past the range it reads zero for free)
       for (int tb = c0; tb < c1; tb += kRing * kBatch) {
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
           const int tr = tb + r * kBatch;
-          load_batch(w[(r + kRing - 1) % kRing], tr + (kRing - 1) * kBatch, c1);
           if (tr < c1) {
+            // every tile of the batch unconditionally (tiles past the range hold zero weights
+            // and add nothing; their plane index is clamped into the array), so the scheduler
+            // can read the next tile's planes while this one is reduced
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-              if (tr + u < c1) {
+              {
                 const u32x4 wc = w[r][u];
+                const int pt = min(tr + u - c0, kChunk - 1);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                  const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[tr + u - c0][m][0]);
+                  const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[pt][m][0]);
                   const u32x4 p0 = X4[0], p1 = X4[1], p2 = X4[2], p3 = X4[3];
                   const uint32_t X[16] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w,
                                           p2.x, p2.y, p2.z, p2.w, p3.x, p3.y, p3.z, p3.w};
@@ -303,6 +342,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
               }
             }
           }
+          load_batch(w[r], tr - t0 + kRing * kBatch);
         }
       }
     }
@@ -336,7 +376,8 @@ GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
   // measured on MI355X: narrow outputs do best with fewer, longer workgroups (every
   // workgroup reads the whole row for gamma), wide ones with more
   const int64_t target = g_gemvf_wg_target ? g_gemvf_wg_target : (bands < 512 ? 256 : 512);
-  int64_t nsplit = (target + groups / 2) / groups;
+  int64_t nsplit = target / groups;   // never above the target: a partial extra wave of
+                                      // workgroups would run after all the others
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kBatch));
   nsplit = std::max<int64_t>(nsplit, 1);
   if (static_cast<int64_t>(M) * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
@@ -403,13 +444,15 @@ hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wp
   const int64_t gl = (K / 8 + 64 * kFW - 1) / (64 * kFW);
   switch (M) {
     case 1:
-      if (gl <= 4) BL_GEMVF_LAUNCH(1, 4);
+      if (gl <= 2) BL_GEMVF_LAUNCH(1, 2);
+      else if (gl <= 4) BL_GEMVF_LAUNCH(1, 4);
       else if (gl <= 8) BL_GEMVF_LAUNCH(1, 8);
       else if (gl <= 16) BL_GEMVF_LAUNCH(1, 16);
       else BL_GEMVF_LAUNCH(1, 0);
       break;
     case 2:
-      if (gl <= 4) BL_GEMVF_LAUNCH(2, 4);
+      if (gl <= 2) BL_GEMVF_LAUNCH(2, 2);
+      else if (gl <= 4) BL_GEMVF_LAUNCH(2, 4);
       else if (gl <= 8) BL_GEMVF_LAUNCH(2, 8);
       else BL_GEMVF_LAUNCH(2, 0);
       break;

@@ -240,6 +240,59 @@ def test_forward_fused_gemv_exact_integers():
     assert np.all(np.isnan(y[2]))
 
 
+def _fused_q(x, packed_eye, K):
+    """Run the fused quantise + GEMV over an identity weight matrix with beta = 1, where
+    y = q * fp32(gamma / 127) exactly up to one rounding, and recover q (exact: |q| <= 127)."""
+    one = dev(np.array([1.0], np.float32))
+    y = host(tw.bl_bitlinear_forward(dev(x), packed_eye, one, K, path=tw.BL_PATH_GEMV))
+    _, rg, _ = oracle.quant_act_int8(x)
+    scale = (rg / np.float32(127)).astype(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return y, np.rint(y.astype(np.float64) / scale[:, None])
+
+
+@pytest.mark.parametrize("M,K", [(1, 8192), (2, 8192), (3, 2048), (4, 2048)])
+def test_forward_fused_quantiser_exhaustive(M, K):
+    """The fused kernel quantises x itself; every finite fp16 x against a ladder of gamma
+    values (rows [x..., gamma]) must give the oracle's q to the bit, including quotients
+    that are exact half-integers (ties to even) and ones within an ulp of them."""
+    eye = dev(np.eye(K, dtype=np.int8))
+    packed = tw.bl_pack_ternary(eye)
+    del eye
+    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite = all16[np.isfinite(all16)]
+    ladder = [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
+              np.float16(3.14), np.float16(127.0)]
+    if M > 2:
+        ladder = ladder[:3]
+    for gamma in ladder:
+        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
+        per = K - 1
+        rows = [xs[i:i + per] for i in range(0, xs.size, per)]
+        say("fused quant exhaustive", M, K, gamma, xs.size, len(rows))
+        for r0 in range(0, len(rows), M):
+            x = np.zeros((M, K), np.float16)
+            x[:, K - 1] = gamma
+            for m, chunk in enumerate(rows[r0:r0 + M]):
+                x[m, :chunk.size] = chunk
+            rq, _, _ = oracle.quant_act_int8(x)
+            _, q = _fused_q(x, packed, K)
+            assert np.array_equal(q, rq.astype(np.float64)), (gamma, r0)
+    # degenerate rows: all zero, one NaN, one inf, all -65504
+    x = synth.normal_fp16((M, K), 0, 94, 1)
+    x[0] = 0
+    if M > 1:
+        x[1, 17] = np.float16(np.inf if M > 2 else np.nan)
+    y, q = _fused_q(x, packed, K)
+    rq, rg, _ = oracle.quant_act_int8(x)
+    assert np.array_equal(y[0], np.zeros(K, np.float32))
+    for m in range(1, M):
+        if np.isnan(rg[m]):
+            assert np.all(np.isnan(y[m]))
+        else:
+            assert np.array_equal(q[m], rq[m].astype(np.float64))
+
+
 def test_config1_tiny_end_to_end():
     """x fp16 [8, 512] ~ N(0,1), W fp32 [512, 512] ~ N(0, 0.02^2), seed 0, both paths."""
     say("config1 tiny")
