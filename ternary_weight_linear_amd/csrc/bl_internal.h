@@ -119,6 +119,23 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// q = rint(a / g) for a = x * 127 (exact in fp32) and |a| <= 127 g, decided on the correctly
+// rounded fp32 quotient. d = a * rcp(g) is within 3.1e-5 of that quotient (rcp 1 ulp, product
+// 0.5 ulp, |a / g| <= 127), so the two round to the same integer unless a half-integer lies
+// within that distance of d; such inputs (fractional part within 2^-12 of 1/2) take the IEEE
+// division instead (behind a wave-uniform test, so that the common case skips it).
+__device__ __forceinline__ int quant_q(float a, float g, float rg) {
+  float d = a * rg;
+  const bool near = fabsf(__builtin_amdgcn_fractf(d) - 0.5f) < 0x1p-12f;
+  if (__ballot(near) != 0) {
+    float gv = g;
+    asm volatile("" : "+v"(gv));   // keeps the division inside the branch (no speculation)
+    const float e = a / gv;
+    d = near ? e : d;
+  }
+  return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d), -127.0f, 127.0f));
+}
+
 // popcount(x) + acc in one v_bcnt_u32_b32 (its second operand accumulates). Written out:
 // the compiler sums pairs of popcounts with a three-input add instead, one more VALU op
 // per pair in the add-only loops.

@@ -152,22 +152,6 @@ constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chu
 static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit elements
 
-// q = rint(a / g) for a = x * 127 (exact in fp32) and |a| <= 127 g, decided on the correctly
-// rounded fp32 quotient. d = a * rcp(g) is within 3.1e-5 of that quotient (rcp 1 ulp, product
-// 0.5 ulp, |a / g| <= 127), so the two round to the same integer unless a half-integer lies
-// within that distance of d; such inputs (fractional part within 2^-12 of 1/2) take the IEEE
-// division instead (behind a wave-uniform test, so that the common case skips it).
-__device__ __forceinline__ int quant_q(float a, float g, float rg) {
-  float d = a * rg;
-  const bool near = fabsf(__builtin_amdgcn_fractf(d) - 0.5f) < 0x1p-12f;
-  if (__ballot(near) != 0) {
-    float gv = g;
-    asm volatile("" : "+v"(gv));   // keeps the division inside the branch (no speculation)
-    const float e = a / gv;
-    d = near ? e : d;
-  }
-  return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d), -127.0f, 127.0f));
-}
 
 template <int MR, int GL>
 __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(

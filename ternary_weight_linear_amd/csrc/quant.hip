@@ -3,7 +3,9 @@
 // [b158] "BitNet b1.58 介绍": activations are scaled per token into [-Q_b, Q_b] with no
 // zero point (the [0, Q_b] variant of the original BitNet is dropped). Reading used here:
 // Q_b = 127, gamma = max |x| over the token, q = clip(rne(fl32(127 x) / gamma)); 127 x is
-// exact in fp32 for fp16 x, so the fp32 division is the only rounding.
+// exact in fp32 for fp16 x, so the fp32 division is the only rounding (its correctly rounded
+// result decides q; quant_q forms it from a reciprocal and falls back to the IEEE division
+// where the two could round apart).
 //
 // One workgroup per token row. Pass 1 copies the fp16 row into LDS while reducing |x| to
 // gamma with wavefront reductions. Pass 2 gives each wave one 64-input tile at a time:
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_kernel(const uint16_t* __rest
   const float g = bad ? __uint_as_float(0x7FC00000u) : mx;
   if (threadIdx.x == 0) gamma[m] = g;
   const bool zero = bad || mx == 0.0f;
+  const float rg = __builtin_amdgcn_rcpf(zero ? 1.0f : g);
 
   // Pass 2. Lane l <-> bit l of the tile's 64-bit plane mask: h = l / 32, bit p = l % 32
   // = 8i + j  <->  input c = 4j + i of half h.
@@ -70,12 +73,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_kernel(const uint16_t* __rest
   int sum = 0;
   for (int64_t t = wave; t < KT; t += NW) {
     const int64_t k = 64 * t + koff;
-    int qv = 0;
-    if (!zero) {
-      const float v = half_bits_to_float(xs[k]) * 127.0f;      // exact
-      const float r = rintf(v / g);                            // IEEE division, RNE
-      qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
-    }
+    const int qv = zero ? 0 : quant_q(half_bits_to_float(xs[k]) * 127.0f, g, rg);
     sum += qv;
     if (q) q[m * K + k] = static_cast<int8_t>(qv);
     if (planes) {
@@ -110,8 +108,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
                                                                int64_t K, int8_t* __restrict__ q,
                                                                float* __restrict__ gamma,
                                                                int32_t* __restrict__ rowsum) {
-  __shared__ float red_max[BLOCK / 64];
-  __shared__ int red_bad[BLOCK / 64];
+  __shared__ uint32_t red_max[BLOCK / 64];
   __shared__ int red_sum[BLOCK / 64];
   constexpr int NW = BLOCK / 64;
   const int64_t m = blockIdx.x;
@@ -122,33 +119,27 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
   uint4 v[NV];
 #pragma unroll
   for (int n = 0; n < NV; ++n) v[n] = row4[min<int64_t>(threadIdx.x + BLOCK * n, K8 - 1)];
-  float mx = 0.0f;
-  int bad = 0;
+  // gamma: for finite fp16 the magnitude order is the integer order of the bits with the
+  // sign cleared, so this is an integer max (>= 0x7C00 flags NaN/inf)
+  uint32_t mb = 0;
 #pragma unroll
   for (int n = 0; n < NV; ++n) {
     const uint32_t w[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint16_t lo = static_cast<uint16_t>(w[j] & 0xFFFFu), hi = static_cast<uint16_t>(w[j] >> 16);
-      bad |= ((lo & 0x7C00u) == 0x7C00u) | ((hi & 0x7C00u) == 0x7C00u);
-      mx = fmaxf(mx, fabsf(half_bits_to_float(lo)));
-      mx = fmaxf(mx, fabsf(half_bits_to_float(hi)));
-    }
+    for (int j = 0; j < 4; ++j) mb = max(mb, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mx = fmaxf(mx, __shfl_xor(mx, off));
-    bad |= __shfl_xor(bad, off);
-  }
-  if (lane == 0) { red_max[wave] = mx; red_bad[wave] = bad; }
+  for (int off = 32; off > 0; off >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, off)));
+  if (lane == 0) red_max[wave] = mb;
   __syncthreads();
-  mx = red_max[0];
-  bad = red_bad[0];
+  mb = red_max[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) { mx = fmaxf(mx, red_max[w]); bad |= red_bad[w]; }
-  const float g = bad ? __uint_as_float(0x7FC00000u) : mx;
+  for (int w = 1; w < NW; ++w) mb = max(mb, red_max[w]);
+  const bool bad = mb >= 0x7C00u;
+  const float g = bad ? __uint_as_float(0x7FC00000u) : half_bits_to_float(static_cast<uint16_t>(mb));
   if (threadIdx.x == 0) gamma[m] = g;
-  const bool zero = bad || mx == 0.0f;
+  const bool zero = bad || mb == 0u;
+  const float rg = __builtin_amdgcn_rcpf(zero ? 1.0f : g);
 
   int sum = 0;
 #pragma unroll
@@ -160,11 +151,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint16_t hb = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      int qv = 0;
-      if (!zero) {
-        const float r = rintf(half_bits_to_float(hb) * 127.0f / g);   // exact product, IEEE division
-        qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
-      }
+      const int qv = zero ? 0 : quant_q(half_bits_to_float(hb) * 127.0f, g, rg);
       sum += qv;
       packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * (e & 3));
     }

@@ -392,11 +392,8 @@ __global__ __launch_bounds__(64 * kSW) void gemv_stack_kernel(StackHeader* __res
       if (tt < c.cend) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          int qv = 0;
-          if (!zero[m]) {
-            const float r = rintf(half_bits_to_float(xq[j][m]) * 127.0f / gam[m]);
-            qv = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
-          }
+          const int qv = zero[m] ? 0 : quant_q(half_bits_to_float(xq[j][m]) * 127.0f, gam[m],
+                                               __builtin_amdgcn_rcpf(gam[m]));
           uint32_t mine = 0;
 #pragma unroll
           for (int b = 0; b < 8; ++b) {
