@@ -330,6 +330,155 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
   tern_epilogue<FM>(a, acc, red, lane, band, m0, nsplit, rowsum);
 }
 
+// ---- T2-MF64 with q staged in LDS (batched decode) --------------------------------------
+// A workgroup of four waves owns four consecutive bands (one per wave), up to 64 rows of q
+// (more rows take more workgroups along y) and a K range. For each chunk of kQC tiles the
+// workgroup copies q[rows, chunk] into LDS once; each wave decodes its own weight tile once
+// (28 ALU ops) and runs FM x 4 MFMAs with A fragments read from LDS, so neither the q bytes
+// nor the decoding are repeated per 16 rows. Weights come through a buffer resource over
+// the wave's band and K range: past the range a load returns zero without a memory access,
+// and a zero code adds nothing to sum q (w + 1), so the ring of R chunks is refilled
+// unconditionally as soon as a slot is consumed. A chunk's q is loaded into registers
+// together with its weights (R chunks ahead) and stored to LDS the step before its use:
+// vector loads complete in issue order, so loading it later would make the store wait for
+// the whole ring. Staged rows are kQC * 64 + 16 bytes apart: the copy and the fragment
+// reads are both free of LDS bank conflicts.
+constexpr int kQC = 4;                     // tiles per q chunk and per weight batch
+constexpr int kQPitch = kQC * 64 + 16;     // bytes per staged row of q
+// chunks in flight per wave: four, three where 48-64 rows of q leave fewer registers
+constexpr int mfq_ring(int fm) { return fm <= 2 ? 4 : 3; }
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elements
+
+template <int FM>
+__global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
+                                                       const int32_t* __restrict__ rowsum) {
+  constexpr int kRows = 16 * FM;
+  constexpr int R = mfq_ring(FM);
+  constexpr int kSegs = kRows * kQC * 4 / 256;   // 16-byte pieces of q per thread per chunk
+  static_assert(kSegs >= 1 && (kRows * kQC * 4) % 256 == 0, "q chunk copy");
+  __shared__ __attribute__((aligned(16))) int8_t qs[2][kRows * kQPitch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, u = lane & 15;
+  const int64_t bands = a.N / 64;
+  const int64_t band = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const bool active = band < bands;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRows;
+  const int split = blockIdx.z, nsplit = gridDim.z;
+  const int KT = static_cast<int>(a.K / 64);
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(KT, t0 + a.tiles_per_split);
+  const int nch = (t1 - t0 + kQC - 1) / kQC;
+
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(a.W + ((active ? band : 0) * KT + t0) * 64), 0,
+      active ? (t1 - t0) * 1024 : 0, kRsrcWord3);
+  u32x4 w[R][kQC];
+  auto load_w = [&](u32x4 (&dst)[kQC], int chunk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kQC; ++t)
+      dst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wr, (chunk * kQC + t) * 1024 + lane * 16, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);   // keep each batch where it is issued
+  };
+  // q piece s = tid + 256 i of a chunk: row s / (4 kQC), tile (s / 4) % kQC, 16 bytes s % 4.
+  // Rows past M and tiles past K are clamped into q (their products are never stored or
+  // meet zero weights).
+  u32x4 qr[R][kSegs];
+  auto load_q = [&](u32x4 (&dst)[kSegs], int chunk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int sg = tid + 256 * i;
+      const int64_t row = min<int64_t>(m0 + sg / (4 * kQC), a.M - 1);
+      const int tile = min(t0 + chunk * kQC + (sg / 4) % kQC, KT - 1);
+      dst[i] = *reinterpret_cast<const u32x4*>(a.q + row * a.K + tile * 64 + (sg % 4) * 16);
+    }
+  };
+  auto store_q = [&](const u32x4 (&src)[kSegs], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int sg = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&qs[buf][(sg / (4 * kQC)) * kQPitch + ((sg / 4) % kQC) * 64 +
+                                         (sg % 4) * 16]) = src[i];
+    }
+  };
+
+  i32x4 acc[FM][4];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[fm][f] = i32x4{0, 0, 0, 0};
+  auto compute = [&](const u32x4 (&wb)[kQC], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kQC; ++t) {
+      const uint32_t w4[4] = {wb[t].x, wb[t].y, wb[t].z, wb[t].w};
+      i32x4 b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[f][j] = static_cast<int>((w4[f] >> (2 * j)) & 0x03030303u);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const i32x4 av = *reinterpret_cast<const i32x4*>(
+            &qs[buf][(16 * fm + u) * kQPitch + t * 64 + g * 16]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b[f], acc[fm][f], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    load_q(qr[r], r);
+    load_w(w[r], r);
+  }
+  store_q(qr[0], 0);
+  __syncthreads();
+  // chunk c: weights and q registers in ring slot c % R, q in LDS buffer c % 2. Step c
+  // reduces chunk c, reloads its slot with chunk c + R, stores chunk c + 1's q, one barrier.
+  for (int c0 = 0; c0 < nch; c0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = c0 + r;
+      if (c < nch) compute(w[r], c & 1);
+      load_q(qr[r], c + R);
+      load_w(w[r], c + R);
+      store_q(qr[(r + 1) % R], (c + 1) & 1);
+      __syncthreads();
+    }
+  }
+  if (!active) return;
+
+  // output k = 4 f + i of row tile fm: row m0 + 16 fm + 4g + i, column band * 64 + 16 f + u
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    int32_t v[16];
+    uint32_t live = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = acc[fm][k / 4][k % 4];
+      if (m0 + 16 * fm + 4 * g + k % 4 < a.M) live |= 1u << k;
+    }
+    auto word = [&](int k) __attribute__((always_inline)) {
+      const int64_t row = min<int64_t>(m0 + 16 * fm + 4 * g + k % 4, a.M - 1);
+      return a.ws_acc + row * a.N + band * 64 + 16 * (k / 4) + u;
+    };
+    const uint32_t done = nsplit > 1 ? split_arrive_batch<16>(word, v, live, nsplit) : live;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (!((done >> k) & 1u)) continue;
+      const int64_t row = m0 + 16 * fm + 4 * g + k % 4;
+      const int64_t col = band * 64 + 16 * (k / 4) + u;
+      const int r = v[k] - rowsum[row];
+      if (a.acc_out) a.acc_out[row * a.N + col] = r;
+      if (a.y)
+        a.y[row * a.N + col] = static_cast<float>(r) * (a.gamma[row] / 127.0f) *
+                               a.beta[a.beta_len == 1 ? 0 : col];
+    }
+  }
+}
+
 struct TernPlan { int64_t bands, mgroups, nsplit, tps; int fm; bool split; };
 
 }  // namespace
@@ -362,15 +511,25 @@ TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-// Workgroups the T2-MF64 kernel aims for (0: 512); tuning harnesses only.
+// Tuning knobs (harnesses that compile this file directly): workgroups the T2-MF64 kernels
+// aim for (0: by kernel) and the kernel (0: by shape, 1: q staged in LDS, 2: per band).
 int64_t g_mf_wg_target = 0;
+int g_mf_kernel = 0;
 
-hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+namespace {
+
+TernArgs mf_args(const int8_t* q, const float* gamma, const void* wmf, const float* beta,
+                 int64_t beta_len, int64_t M, int64_t N, int64_t K, float* y, int32_t* acc_out,
+                 uint64_t* ws_acc, int64_t tps) {
+  return TernArgs{q, gamma, static_cast<const u32x4*>(wmf), beta, beta_len, M, N, K, y,
+                  acc_out, ws_acc, static_cast<int>(tps)};
+}
+
+// Per-band kernel: one 16-row tile of q per workgroup, K split until ~512 workgroups.
+hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
-                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
-  // measured on MI355X (70B-shaped decode, M = 8..64): one 16-row tile of q per wave and
-  // many workgroups beat wider tiles that read each weight once (the extra weight reads
-  // cost less than the lost parallelism); K is split until ~512 workgroups
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
+                          hipStream_t s) {
   const int64_t KT = K / 64, bands = N / 64;
   const int64_t mgroups = (M + 15) / 16;
   const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 512;
@@ -382,12 +541,60 @@ hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* ro
   int64_t tps = (KT + nsplit - 1) / nsplit;
   nsplit = (KT + tps - 1) / tps;
   if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
-  TernArgs a{q, gamma, static_cast<const u32x4*>(wmf), beta, beta_len, M, N, K, y, acc_out,
-             ws_acc, static_cast<int>(tps)};
+  const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, tps);
   const dim3 grid(static_cast<unsigned>(bands), static_cast<unsigned>(mgroups),
                   static_cast<unsigned>(nsplit));
   hipLaunchKernelGGL((tern_mf_kernel<1>), grid, dim3(256), 0, s, a, rowsum);
   return hipGetLastError();
+}
+
+// Staged-q kernel: four bands and up to 64 rows per workgroup.
+hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
+                          hipStream_t s) {
+  const int64_t KT = K / 64, bands = N / 64, groups = (bands + 3) / 4;
+  const int fm = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
+  const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
+  // K is split until about `target` workgroups; a split spans whole ring turns where the
+  // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
+  const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 256;
+  int64_t nsplit = std::max<int64_t>(1, target / (groups * mgroups));
+  const int64_t turn = kQC * mfq_ring(fm);
+  int64_t tps = (KT + nsplit - 1) / nsplit;
+  tps = std::min<int64_t>((tps + turn - 1) / turn * turn, kMfMaxSplitTiles / turn * turn);
+  nsplit = (KT + tps - 1) / tps;
+  if (M * N > kAccCap) nsplit = 1;
+  if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
+  // (nsplit <= KT / 12 <= 86 < kMaxIntSplits: a split word never overflows its count)
+  const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, tps);
+  const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(mgroups),
+                  static_cast<unsigned>(nsplit));
+  switch (fm) {
+    case 1: hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum); break;
+    case 2: hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum); break;
+    case 3: hipLaunchKernelGGL((tern_mfq_kernel<3>), grid, dim3(256), 0, s, a, rowsum); break;
+    default: hipLaunchKernelGGL((tern_mfq_kernel<4>), grid, dim3(256), 0, s, a, rowsum); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
+  // measured on MI355X (70B-shaped decode, M = 8..64): outputs of >= 192 four-band groups
+  // fill the GPU without splitting K and take the staged-q kernel (each weight tile read
+  // and decoded once for all rows; gate|up at M = 64: 55 us against 90 us); narrower ones
+  // would need K splits whose split-word atomics (M x N per split) cost more than the
+  // per-band kernel's repeated weight reads, and take that
+  const int64_t groups = (N / 64 + 3) / 4;
+  const bool quad = g_mf_kernel == 1 || (g_mf_kernel == 0 && groups >= 192);
+  return quad ? launch_mf_quad(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,
+                               ws_acc, s)
+              : launch_mf_band(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,
+                               ws_acc, s);
 }
 
 hipError_t launch_tern_mfma(const int8_t* q, const float* gamma, int64_t M, int64_t K,
