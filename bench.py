@@ -77,11 +77,17 @@ def timed(torch, fn, steps, warmup):
 def build_stack70b(torch, tw, sgpu, synth, dev):
     """80 layers of packed ternary weights, stacked per dependent group (N-concatenation of
     T2-PN-64 buffers is the packed form of the stacked matrix)."""
-    shapes = dict((n, (N, K)) for n, N, K in synth.LLAMA70B_LINEARS)
+    return build_stack(torch, tw, sgpu, synth, dev, synth.LLAMA70B_LINEARS, synth.LLAMA70B_LAYERS, 5)
+
+
+def build_stack(torch, tw, sgpu, synth, dev, linears, nlayers, key_id):
+    """nlayers layers of the given linears, packed and stacked per dependent group: q|k|v and
+    gate|up share their input, so each pair or triple is one matrix of stacked rows."""
+    shapes = dict((n, (N, K)) for n, N, K in linears)
     groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
     tmp = torch.empty(max(N * K for N, K in shapes.values()), dtype=torch.int8, device=dev)
     layers = []
-    for layer in range(synth.LLAMA70B_LAYERS):
+    for layer in range(nlayers):
         lg = []
         for gname, members in groups:
             K = shapes[members[0]][1]
@@ -90,8 +96,8 @@ def build_stack70b(torch, tw, sgpu, synth, dev):
             off = 0
             for m in members:
                 N = shapes[m][0]
-                mid = [n for n, _, _ in synth.LLAMA70B_LINEARS].index(m)
-                key = synth.matrix_key(0, 5, layer, mid)
+                mid = [n for n, _, _ in linears].index(m)
+                key = synth.matrix_key(0, key_id, layer, mid)
                 codes = tmp[: N * K].view(N, K)
                 sgpu.ternary_codes(key, N, K, dev, out=codes)
                 st = tw._lib.bl_pack_ternary(tw._ptr(codes), N, K, tw.ctypes.c_void_p(buf.data_ptr() + off),
@@ -286,8 +292,20 @@ def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
                 frac_peak_gemms=ops / (ms_g / 1e3) / 1e12 / INT8_PEAK_TOPS, per_shape=per_shape)
 
 
+def bench_decode7b_stack(torch, tw, sgpu, synth, dev, steps, warmup):
+    """The LLaMA-7B-shaped model decoded at M = 1: 32 layers (1.62 GB packed, > the 256 MB
+    MALL) in model order, q|k|v and gate|up stacked, one fused quantise + GEMV launch per
+    group, replayed from a HIP graph (the same pass as the 70B line)."""
+    layers = build_stack(torch, tw, sgpu, synth, dev, synth.LLAMA7B_LINEARS, 32, 3)
+    r = bench_decode70b(torch, tw, synth, dev, layers, 1, steps, warmup)
+    del layers
+    return {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs", "launches_per_pass", "weight_bytes")}
+
+
 def bench_decode7b(torch, tw, sgpu, synth, dev, steps, warmup, pool=32):
-    """7B-shaped set of 7 linears at M = 1, a pool of `pool` distinct sets (> the 256 MB MALL)."""
+    """7B-shaped set of 7 linears at M = 1, a pool of `pool` distinct sets (> the 256 MB MALL),
+    each its own bl_bitlinear_gemv launch on bit planes quantised beforehand (the standalone
+    GEMV entry point, no stacking)."""
     M = 1
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=dev)
     items = []
@@ -498,9 +516,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": a.numel()}))
         return
 
-    if args.only in ("prefill3b", "decode7b", "onebit", "residual"):
+    if args.only in ("prefill3b", "decode7b", "decode7b_stack", "onebit", "residual"):
         fn = {"prefill3b": lambda: bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup),
               "decode7b": lambda: bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup),
+              "decode7b_stack": lambda: bench_decode7b_stack(torch, tw, sgpu, synth, dev, args.steps, args.warmup),
               "onebit": lambda: bench_onebit(torch, tw, synth, dev, args.steps, args.warmup),
               "residual": lambda: bench_residual(torch, tw, synth, dev, args.steps, args.warmup)}[args.only]
         print(json.dumps({args.only: fn()}))
@@ -553,8 +572,10 @@ def main():
     if not args.skip_extra:
         extra["prefill3b_m512"] = bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup)
         log("prefill3b:", json.dumps(extra["prefill3b_m512"]))
+        extra["decode7b_m1"] = bench_decode7b_stack(torch, tw, sgpu, synth, dev, args.steps, args.warmup)
+        log("decode7b (32 layers, stacked, fused):", json.dumps(extra["decode7b_m1"]))
         extra["decode7b_m1_pool32"] = bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup)
-        log("decode7b:", json.dumps(extra["decode7b_m1_pool32"]))
+        log("decode7b (7 GEMV launches per layer):", json.dumps(extra["decode7b_m1_pool32"]))
         extra["onebit4096_pool256"] = bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)
         extra["residual4096_pool128"] = bench_residual(torch, tw, synth, dev, args.steps, args.warmup)
         log("onebit:", json.dumps(extra["onebit4096_pool256"]))
