@@ -345,6 +345,7 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
 // reads are both free of LDS bank conflicts.
 constexpr int kQC = 4;                     // tiles per q chunk and per weight batch
 constexpr int kQPitch = kQC * 64 + 16;     // bytes per staged row of q
+constexpr int kStRow = 68;                 // ints per staged result row (64 + 4)
 // chunks in flight per wave: four, three where 48-64 rows of q leave fewer registers
 constexpr int mfq_ring(int fm) { return fm <= 2 ? 4 : 3; }
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elements
@@ -356,16 +357,32 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
   constexpr int R = mfq_ring(FM);
   constexpr int kSegs = kRows * kQC * 4 / 256;   // 16-byte pieces of q per thread per chunk
   static_assert(kSegs >= 1 && (kRows * kQC * 4) % 256 == 0, "q chunk copy");
-  __shared__ __attribute__((aligned(16))) int8_t qs[2][kRows * kQPitch];
+  constexpr int kQBuf = kRows * kQPitch;           // one staged chunk of q
+  constexpr int kLds = 2 * kQBuf > 4 * 16 * kStRow * 4 ? 2 * kQBuf : 4 * 16 * kStRow * 4;
+  __shared__ __attribute__((aligned(16))) int8_t lds[kLds];   // q chunks, then results
+  auto qs = [&](int buf) __attribute__((always_inline)) { return lds + buf * kQBuf; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, u = lane & 15;
   const int64_t bands = a.N / 64;
-  const int64_t band = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const bool active = band < bands;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRows;
-  const int split = blockIdx.z, nsplit = gridDim.z;
   const int KT = static_cast<int>(a.K / 64);
+  // Work item of this workgroup. Dispatch ids are dealt round-robin over the 8 XCDs (id i
+  // runs on XCD i % 8); each XCD takes a contiguous range of work items, ordered split,
+  // band group, row group (fastest), so the row groups of a band group run side by side on
+  // one XCD and read its weights through that XCD's L2 once instead of once per row group.
+  const int groups = static_cast<int>((bands + 3) / 4);
+  const int mgroups = static_cast<int>((a.M + kRows - 1) / kRows);
+  const int nsplit = (KT + a.tiles_per_split - 1) / a.tiles_per_split;
+  const int nwork = groups * mgroups * nsplit;
+  const int per_xcd = (nwork + 7) / 8;
+  const int wk = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
+  if (wk >= nwork) return;   // the grid is rounded up to 8 per_xcd
+  const int mg = wk % mgroups;
+  const int grp = (wk / mgroups) % groups;
+  const int split = wk / (mgroups * groups);
+  const int64_t band = static_cast<int64_t>(grp) * 4 + wave;
+  const bool active = band < bands;
+  const int64_t m0 = static_cast<int64_t>(mg) * kRows;
   const int t0 = split * a.tiles_per_split;
   const int t1 = min(KT, t0 + a.tiles_per_split);
   const int nch = (t1 - t0 + kQC - 1) / kQC;
@@ -398,8 +415,8 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
       const int sg = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(&qs[buf][(sg / (4 * kQC)) * kQPitch + ((sg / 4) % kQC) * 64 +
-                                         (sg % 4) * 16]) = src[i];
+      *reinterpret_cast<u32x4*>(qs(buf) + (sg / (4 * kQC)) * kQPitch + ((sg / 4) % kQC) * 64 +
+                                (sg % 4) * 16) = src[i];
     }
   };
 
@@ -420,7 +437,7 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const i32x4 av = *reinterpret_cast<const i32x4*>(
-            &qs[buf][(16 * fm + u) * kQPitch + t * 64 + g * 16]);
+            qs(buf) + (16 * fm + u) * kQPitch + t * 64 + g * 16);
 #pragma unroll
         for (int f = 0; f < 4; ++f)
           acc[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b[f], acc[fm][f], 0, 0, 0);
@@ -447,6 +464,41 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
       store_q(qr[(r + 1) % R], (c + 1) & 1);
       __syncthreads();
     }
+  }
+  // Without a K split the integers leave through LDS as whole rows: each wave stages its
+  // 16 x 64 slice of row tile fm (rows kStRow ints apart: conflict-free both ways), then
+  // writes it back row by row, lane = column, so every store covers 256 contiguous bytes
+  // (from the MFMA layout directly, a store covers four 64-byte pieces of four rows).
+  if (nsplit == 1) {
+    __syncthreads();                        // every wave is done with the q chunks
+    int* st = reinterpret_cast<int*>(lds) + wave * 16 * kStRow;
+    const int64_t col = band * 64 + lane;
+    const float bcol = (a.y != nullptr && active) ? a.beta[a.beta_len == 1 ? 0 : col] : 0.0f;
+    // row sums and scales of the workgroup's rows, lane l holding row m0 + l (clamped), read
+    // by every row below as a wave-uniform value
+    const int64_t rl = min<int64_t>(m0 + lane, a.M - 1);
+    const int rs_l = rowsum[rl];
+    const float gs_l = a.y != nullptr ? a.gamma[rl] / 127.0f : 0.0f;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)   // output k: row 4g + k % 4, column 16 (k / 4) + u
+        st[(4 * g + k % 4) * kStRow + 16 * (k / 4) + u] = acc[fm][k / 4][k % 4];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 16 * fm + r;
+        const int v = st[r * kStRow + lane] - __builtin_amdgcn_readlane(rs_l, rr);
+        const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs_l), rr));
+        const int64_t row = m0 + rr;
+        if (active && row < a.M) {
+          if (a.acc_out) a.acc_out[row * a.N + col] = v;
+          if (a.y) a.y[row * a.N + col] = static_cast<float>(v) * gs * bcol;
+        }
+      }
+      __syncthreads();
+    }
+    return;
   }
   if (!active) return;
 
@@ -568,8 +620,8 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
   // (nsplit <= KT / 12 <= 86 < kMaxIntSplits: a split word never overflows its count)
   const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, tps);
-  const dim3 grid(static_cast<unsigned>(groups), static_cast<unsigned>(mgroups),
-                  static_cast<unsigned>(nsplit));
+  const int64_t nwork = groups * mgroups * nsplit;   // one workgroup per item, 8 | grid
+  const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
   switch (fm) {
     case 1: hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum); break;
     case 2: hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum); break;
