@@ -567,6 +567,7 @@ TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
 // aim for (0: by kernel) and the kernel (0: by shape, 1: q staged in LDS, 2: per band).
 int64_t g_mf_wg_target = 0;
 int g_mf_kernel = 0;
+int g_mf_fm = 0;   // 16-row tiles of q per workgroup of the staged-q kernel (0: by M)
 
 namespace {
 
@@ -600,13 +601,22 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
   return hipGetLastError();
 }
 
-// Staged-q kernel: four bands and up to 64 rows per workgroup.
+// Row tile of the staged-q kernel (16 fm rows per workgroup), measured on MI355X
+// (70B-shaped batched decode, 3B-shaped prefill): 32 rows for 17..64 rows of q where that
+// still gives >= 192 workgroups (the decoded weights serve more rows), else 16 (row groups
+// of a band group share its weights through one XCD's L2, and more workgroups win).
+int mfq_fm(int64_t M, int64_t groups) {
+  if (g_mf_fm > 0) return g_mf_fm;
+  return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
+}
+
+// Staged-q kernel: four bands and 16 fm rows per workgroup.
 hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
                           hipStream_t s) {
   const int64_t KT = K / 64, bands = N / 64, groups = (bands + 3) / 4;
-  const int fm = M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 4;
+  const int fm = mfq_fm(M, groups);
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
   // K is split until about `target` workgroups; a split spans whole ring turns where the
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
@@ -636,13 +646,14 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
 hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
-  // measured on MI355X (70B-shaped decode, M = 8..64): outputs of >= 192 four-band groups
-  // fill the GPU without splitting K and take the staged-q kernel (each weight tile read
-  // and decoded once for all rows; gate|up at M = 64: 55 us against 90 us); narrower ones
-  // would need K splits whose split-word atomics (M x N per split) cost more than the
-  // per-band kernel's repeated weight reads, and take that
+  // measured on MI355X (70B-shaped decode at M = 8..64, 3B-shaped prefill at M = 512): the
+  // staged-q kernel wherever its work items (four-band groups x row tiles) number >= 160,
+  // so that it fills the GPU without splitting K (e.g. gate|up at M = 64: 42 us against 91
+  // us per band; every 3B GEMM at M = 512); with fewer, K splits would cost M x N
+  // split-word atomics per split, more than the per-band kernel's repeated weight reads
   const int64_t groups = (N / 64 + 3) / 4;
-  const bool quad = g_mf_kernel == 1 || (g_mf_kernel == 0 && groups >= 192);
+  const int64_t items = groups * ((M + 16 * mfq_fm(M, groups) - 1) / (16 * mfq_fm(M, groups)));
+  const bool quad = g_mf_kernel == 1 || (g_mf_kernel == 0 && items >= 160);
   return quad ? launch_mf_quad(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,
                                ws_acc, s)
               : launch_mf_band(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,

@@ -658,13 +658,15 @@ def test_mf_invalid_codes():
     assert np.array_equal(host(mf2), oracle.pack_ternary_mf(np.zeros((64, 64), dtype=np.int8)))
 
 
-# N >= 49152 (192 four-band groups and more) takes the staged-q kernel, narrower outputs the
-# per-band one; 49216 leaves a last group with one band, M = 70 two row groups.
+# Four-band groups x row tiles >= 160 take the staged-q kernel (N = 49152, 10240 at M = 200),
+# fewer the per-band one; 49216 leaves a last group with one band; M = 40, 70, 200 ragged
+# row tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 192, 320), (8, 512, 512), (16, 640, 1024),
                                    (17, 384, 448), (33, 256, 640), (64, 1024, 8192),
                                    (100, 256, 640), (2, 128, 39936), (8, 8192, 28672),
                                    (1, 49216, 64), (8, 49152, 256), (40, 49152, 192),
-                                   (64, 49152, 320), (70, 49152, 128), (16, 49152, 1024)])
+                                   (64, 49152, 320), (70, 49152, 128), (16, 49152, 1024),
+                                   (200, 10240, 128), (96, 2560, 256)])
 def test_gemm_mf_acc_and_output(M, N, K):
     say("gemm mf", M, N, K)
     codes = synth.ternary_codes(synth.matrix_key(0, 131, N, K), N, K)
@@ -692,7 +694,7 @@ def test_gemm_mf_acc_and_output(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 512, 512), (32, 320, 1024), (64, 1024, 8192),
-                                   (33, 49152, 256)])
+                                   (33, 49152, 256), (300, 12800, 256)])
 def test_forward_mf_equals_forward(M, N, K):
     """The same weights as T2-MF64 and T2-PN-64 give identical outputs (both kernels sum the
     exact integers and apply one epilogue)."""
