@@ -233,7 +233,9 @@ def bench_decode70b(torch, tw, synth, dev, layers, M, steps, warmup, use_graph=T
 
 def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
     """3B-shaped linears at M = 512: W ~ N(0, 0.02^2) -> absmean ternary on the GPU; x fp16 ~
-    N(0,1) with 1% outlier channels x20. Groups stacked as in the decode pass."""
+    N(0,1) with 1% outlier channels x20. Groups stacked as in the decode pass. Measured with
+    the weights in T2-MF64 (the matrix-core layout, repacked once on the GPU; quantiser with
+    row sums + bl_bitlinear_gemm_mf) and, for comparison, in T2-PN-64 (bl_bitlinear_gemm)."""
     shapes = dict((n, (N, K)) for n, N, K in synth.LLAMA3B_LINEARS)
     groups = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
     M = 512
@@ -253,10 +255,12 @@ def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
         beta = torch.cat(betas).contiguous()
         Ntot = sum(shapes[m][0] for m in members)
         x16, _ = synth.with_outlier_channels(synth.normal_fp16((M, K), 0, 4, 100, gi), 0.01, 20.0, 0, 4, 200 + gi)
-        items.append(dict(x=torch.from_numpy(x16).to(dev), w=w, beta=beta, N=Ntot, K=K,
+        items.append(dict(x=torch.from_numpy(x16).to(dev), w=w, wmf=tw.bl_repack_ternary_mf(w, Ntot, K),
+                          beta=beta, N=Ntot, K=K,
                           y=torch.empty((M, Ntot), dtype=torch.float32, device=dev),
                           q=torch.empty((M, K), dtype=torch.int8, device=dev),
-                          gamma=torch.empty(M, dtype=torch.float32, device=dev)))
+                          gamma=torch.empty(M, dtype=torch.float32, device=dev),
+                          rowsum=torch.empty(M, dtype=torch.int32, device=dev)))
     ws = tw.workspace(dev, max(tw.bl_workspace_bytes(M, it["N"], it["K"]) for it in items))
     wsp, wsb = tw.ctypes.c_void_p(ws.data_ptr()), ws.numel()
     stream = tw._stream(torch.device(dev))
@@ -264,32 +268,38 @@ def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
 
     def quant(it):
         assert lib.bl_quant_act_int8(P(it["x"].data_ptr()), M, it["K"], P(it["q"].data_ptr()),
-                                     P(it["gamma"].data_ptr()), None, None, stream) == 0
+                                     P(it["gamma"].data_ptr()), P(it["rowsum"].data_ptr()), None,
+                                     stream) == 0
 
-    def gemm(it):
+    def gemm_mf(it):
+        assert lib.bl_bitlinear_gemm_mf(P(it["q"].data_ptr()), P(it["gamma"].data_ptr()),
+                                        P(it["rowsum"].data_ptr()), M, it["K"], P(it["wmf"].data_ptr()),
+                                        P(it["beta"].data_ptr()), it["N"], it["N"], P(it["y"].data_ptr()),
+                                        None, wsp, wsb, stream) == 0
+
+    def gemm_pn(it):
         assert lib.bl_bitlinear_gemm(P(it["q"].data_ptr()), P(it["gamma"].data_ptr()), M, it["K"],
                                      P(it["w"].data_ptr()), P(it["beta"].data_ptr()), it["N"], it["N"],
                                      P(it["y"].data_ptr()), wsp, wsb, stream) == 0
 
-    def full():
-        for it in items:
-            quant(it)
-            gemm(it)
-
-    def gemms():
-        for it in items:
-            gemm(it)
-
-    ms = timed(torch, full, steps, warmup)
-    ms_g = timed(torch, gemms, steps, warmup)
     ops = sum(2 * M * it["N"] * it["K"] for it in items)
-    per_shape = {}
-    for it in items:
-        t = timed(torch, lambda it=it: gemm(it), steps, warmup)
-        per_shape[f"{M}x{it['N']}x{it['K']}"] = dict(ms=t, tops=2 * M * it["N"] * it["K"] / (t / 1e3) / 1e12)
-    return dict(ms_per_pass=ms, ms_gemms_only=ms_g, int8_ops=ops, tops_pass=ops / (ms / 1e3) / 1e12,
-                tops_gemms=ops / (ms_g / 1e3) / 1e12,
-                frac_peak_gemms=ops / (ms_g / 1e3) / 1e12 / INT8_PEAK_TOPS, per_shape=per_shape)
+
+    def measure(gemm):
+        ms = timed(torch, lambda: [f(it) for it in items for f in (quant, gemm)], steps, warmup)
+        ms_g = timed(torch, lambda: [gemm(it) for it in items], steps, warmup)
+        per_shape = {}
+        for it in items:
+            t = timed(torch, lambda it=it: gemm(it), steps, warmup)
+            per_shape[f"{M}x{it['N']}x{it['K']}"] = dict(ms=t, tops=2 * M * it["N"] * it["K"] / (t / 1e3) / 1e12)
+        return dict(ms_per_pass=ms, ms_gemms_only=ms_g, int8_ops=ops, tops_pass=ops / (ms / 1e3) / 1e12,
+                    tops_gemms=ops / (ms_g / 1e3) / 1e12,
+                    frac_peak_gemms=ops / (ms_g / 1e3) / 1e12 / INT8_PEAK_TOPS, per_shape=per_shape)
+
+    res = measure(gemm_mf)
+    res["weights"] = "T2-MF64"
+    pn = measure(gemm_pn)
+    res["t2pn"] = {k: pn[k] for k in ("ms_per_pass", "ms_gemms_only", "tops_gemms", "frac_peak_gemms")}
+    return res
 
 
 def bench_decode7b_stack(torch, tw, sgpu, synth, dev, steps, warmup):
