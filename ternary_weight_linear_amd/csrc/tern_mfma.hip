@@ -330,9 +330,9 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
   tern_epilogue<FM>(a, acc, red, lane, band, m0, nsplit, rowsum);
 }
 
-// ---- T2-MF64 with q staged in LDS (batched decode) --------------------------------------
-// A workgroup of four waves owns four consecutive bands (one per wave), up to 64 rows of q
-// (more rows take more workgroups along y) and a K range. For each chunk of kQC tiles the
+// ---- T2-MF64 with q staged in LDS (batched decode, prefill) -----------------------------
+// A workgroup of four waves owns four consecutive bands (one per wave), 16 FM rows of q
+// (FM = 1 or 2; more rows take more workgroups) and a K range. For each chunk of kQC tiles the
 // workgroup copies q[rows, chunk] into LDS once; each wave decodes its own weight tile once
 // (28 ALU ops) and runs FM x 4 MFMAs with A fragments read from LDS, so neither the q bytes
 // nor the decoding are repeated per 16 rows. Weights come through a buffer resource over
@@ -346,15 +346,14 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
 constexpr int kQC = 4;                     // tiles per q chunk and per weight batch
 constexpr int kQPitch = kQC * 64 + 16;     // bytes per staged row of q
 constexpr int kStRow = 68;                 // ints per staged result row (64 + 4)
-// chunks in flight per wave: four, three where 48-64 rows of q leave fewer registers
-constexpr int mfq_ring(int fm) { return fm <= 2 ? 4 : 3; }
+constexpr int kQRing = 4;                  // chunks in flight per wave
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elements
 
 template <int FM>
 __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
                                                        const int32_t* __restrict__ rowsum) {
   constexpr int kRows = 16 * FM;
-  constexpr int R = mfq_ring(FM);
+  constexpr int R = kQRing;
   constexpr int kSegs = kRows * kQC * 4 / 256;   // 16-byte pieces of q per thread per chunk
   static_assert(kSegs >= 1 && (kRows * kQC * 4) % 256 == 0, "q chunk copy");
   constexpr int kQBuf = kRows * kQPitch;           // one staged chunk of q
@@ -606,7 +605,7 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
 // still gives >= 192 workgroups (the decoded weights serve more rows), else 16 (row groups
 // of a band group share its weights through one XCD's L2, and more workgroups win).
 int mfq_fm(int64_t M, int64_t groups) {
-  if (g_mf_fm > 0) return g_mf_fm;
+  if (g_mf_fm > 0) return g_mf_fm > 1 ? 2 : 1;
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 
@@ -622,7 +621,7 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
   const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 256;
   int64_t nsplit = std::max<int64_t>(1, target / (groups * mgroups));
-  const int64_t turn = kQC * mfq_ring(fm);
+  const int64_t turn = kQC * kQRing;
   int64_t tps = (KT + nsplit - 1) / nsplit;
   tps = std::min<int64_t>((tps + turn - 1) / turn * turn, kMfMaxSplitTiles / turn * turn);
   nsplit = (KT + tps - 1) / tps;
@@ -632,12 +631,10 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, tps);
   const int64_t nwork = groups * mgroups * nsplit;   // one workgroup per item, 8 | grid
   const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
-  switch (fm) {
-    case 1: hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum); break;
-    case 2: hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum); break;
-    case 3: hipLaunchKernelGGL((tern_mfq_kernel<3>), grid, dim3(256), 0, s, a, rowsum); break;
-    default: hipLaunchKernelGGL((tern_mfq_kernel<4>), grid, dim3(256), 0, s, a, rowsum); break;
-  }
+  if (fm == 1)
+    hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum);
+  else
+    hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum);
   return hipGetLastError();
 }
 
