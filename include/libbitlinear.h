@@ -67,6 +67,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The library is built with hidden default visibility: the declarations below are its only
+ * exported symbols. */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -313,5 +319,9 @@ int bl_residual_linear(const uint16_t* x, const void* planes_o, const float* alp
 
 #ifdef __cplusplus
 }
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
 #endif
 #endif /* LIBBITLINEAR_H */

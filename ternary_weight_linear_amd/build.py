@@ -43,8 +43,8 @@ def _run(cmd):
     return r.stdout
 
 
-def _compile(src, obj, includes):
-    _run([HIPCC, *COMMON, *[f"-I{i}" for i in includes], "-c", src, "-o", obj])
+def _compile(src, obj, includes, extra=()):
+    _run([HIPCC, *COMMON, *extra, *[f"-I{i}" for i in includes], "-c", src, "-o", obj])
     return obj
 
 
@@ -54,8 +54,11 @@ def build(verbose: bool = False) -> str:
     jobs = []
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
         for s in SOURCES:
+            # hidden by default: only the entry points include/libbitlinear.h declares are
+            # exported (the header marks them visible)
             jobs.append(ex.submit(_compile, os.path.join(CSRC, s),
-                                  os.path.join(BUILD_DIR, s.replace(".hip", ".o")), [CSRC, INCLUDE]))
+                                  os.path.join(BUILD_DIR, s.replace(".hip", ".o")), [CSRC, INCLUDE],
+                                  ["-fvisibility=hidden"]))
         jsyn = ex.submit(_compile, os.path.join(SYNTH_DIR, "csrc", "synth.hip"),
                          os.path.join(BUILD_DIR, "synth.o"), [])
         objs = [j.result() for j in jobs]

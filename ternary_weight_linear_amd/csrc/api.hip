@@ -279,7 +279,6 @@ int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
   char* w = static_cast<char*>(ws);
   return check_launch(launch_gemm(q, gamma, M, K, wpacked, beta, beta_len, N, y, nullptr,
                                   reinterpret_cast<uint64_t*>(w + L.acc_off),
-                                  reinterpret_cast<uint32_t*>(w + L.cnt_off),
                                   static_cast<hipStream_t>(stream)),
                       "bl_bitlinear_gemm");
 }
@@ -372,7 +371,7 @@ int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int
                                     N, nullptr, acc, wsacc, wscnt, s),
                         "bl_bitlinear_acc_i32");
   return check_launch(launch_gemm(q, nullptr, M, K, wpacked, nullptr, 1, N, nullptr, acc, wsacc,
-                                  wscnt, s),
+                                  s),
                       "bl_bitlinear_acc_i32");
 }
 
@@ -406,7 +405,7 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
     auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
     e = launch_quant_act(x, M, K, qbuf, gbuf, nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward (quantise)");
-    e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, wscnt, s);
+    e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, s);
   }
   return check_launch(e, "bl_bitlinear_forward");
 }

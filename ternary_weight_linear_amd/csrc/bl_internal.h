@@ -82,8 +82,7 @@ hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wp
                              uint64_t* ws_acc, uint32_t* ws_cnt, hipStream_t s);
 hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
-                       hipStream_t s);
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s);
 // Residual binarisation: two S1-128 sign planes plus fp32 scales [N, K/128] per plane.
 hipError_t launch_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o,
                                     float* alpha_o, void* planes_r, float* alpha_r,

@@ -9,13 +9,9 @@
 // in bytes 0..3 (the layout's bit order was chosen for this), and
 // (P_bytes) + 255 * (N_bytes) turns flags into int8 +1 / -1 bytes (expand_flags).
 //
-// Work split: a 256-thread workgroup owns a BM x BN output tile (4 waves, each a
-// (BM/WGM) x (BN/WGN) sub-tile of 16 x 16 MFMA fragments) and a range of 64-input k tiles.
 // Batched decode (M <= 64) goes to the weight-streaming kernel of tern_mfma.hip and prefill
-// to the register-blocked kernel below; this tiled kernel remains for tuning comparisons. When K is split across workgroups, partial
+// to the register-blocked kernel below. When K is split across workgroups, partial
 // accumulators meet in the workspace's split words and the last one applies the epilogue.
-// Workgroup ids are remapped so that tiles sharing a weight column block run on the same
-// XCD (ids are dealt round-robin to the 8 XCDs), keeping that block in one L2.
 #include "bl_internal.h"
 
 namespace bl {
@@ -34,153 +30,6 @@ __device__ __forceinline__ uint32_t expand_flags(uint32_t pb, uint32_t nb) {
   uint32_t o;
   asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(o) : "v"(nb), "v"(pb - nb));
   return o;
-}
-
-template <int BM, int BN, int WGM, int S>
-__global__ __launch_bounds__(256) void gemm_kernel(
-    const int8_t* __restrict__ q, const float* __restrict__ gamma, int64_t M, int64_t K,
-    const u32x4* __restrict__ W, const float* __restrict__ beta, int64_t beta_len, int64_t N,
-    float* __restrict__ y, int32_t* __restrict__ acc_out, uint64_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ ws_cnt, int tiles_per_split, int MT, int NT) {
-  constexpr int WGN = 4 / WGM;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  static_assert(FM >= 1 && FN >= 1, "tile too small");
-  constexpr int A_CHUNKS = BM * 4;              // 16-byte chunks of an activation tile
-  constexpr int A_PER = (A_CHUNKS + 255) / 256;
-  constexpr int B_ITEMS = BN * 4;               // (row, half, quarter) expansion items
-  constexpr int B_PER = (B_ITEMS + 255) / 256;
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLd];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLd];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-
-  // XCD-aware tile order: blocks b, b+8, b+16, ... run on one XCD; give them consecutive
-  // logical tiles, which share a weight column block (m varies fastest).
-  const int nblocks = MT * NT;
-  int L = blockIdx.x;
-  if ((nblocks & 7) == 0) L = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
-  const int mt = L % MT, nt = L / MT;
-  const int64_t m0 = static_cast<int64_t>(mt) * BM, n0 = static_cast<int64_t>(nt) * BN;
-  const int KT = static_cast<int>(K / 64);
-  const int t0 = blockIdx.y * tiles_per_split;
-  const int t1 = min(KT, t0 + tiles_per_split);
-
-  // Software pipeline: k tiles are fetched from global memory into registers S tiles ahead
-  // of the one being multiplied, staged (weights expanded to int8) into one of two LDS
-  // buffers, then multiplied; one barrier per k tile. The deep register prefetch hides
-  // the global-load latency, which is far longer than one tile's MFMA work. Every fetch is
-  // unconditional (rows, columns, chunks and k tiles past their ranges are clamped into
-  // range; such values only reach outputs that are never stored): vector loads complete in
-  // issue order, and loads behind branches would make the compiler wait for all of them
-  // instead of for the one tile a step needs.
-  u32x4 ra[S][A_PER];
-  u32x4 rb[S][B_PER];
-  auto fetch = [&](int s, int tk) {
-    tk = min(tk, t1 - 1);
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = min(tid + 256 * i, A_CHUNKS - 1);
-      const int64_t row = min<int64_t>(m0 + (c >> 2), M - 1);
-      ra[s][i] = *reinterpret_cast<const u32x4*>(q + row * K + static_cast<int64_t>(tk) * 64 + (c & 3) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = min(tid + 256 * i, B_ITEMS - 1);
-      const int64_t n = min<int64_t>(n0 + (c >> 2), N - 1);
-      rb[s][i] = W[((n >> 6) * KT + tk) * 64 + (n & 63)];
-    }
-  };
-  auto stage = [&](int s, int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + 256 * i;
-      if (c < A_CHUNKS) *reinterpret_cast<u32x4*>(&As[buf][(c >> 2) * kLd + (c & 3) * 16]) = ra[s][i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + 256 * i;
-      if (c < B_ITEMS) {
-        // item c: tile row c / 4, half hh (inputs 32hh..), quarter qq (16 of those inputs)
-        const int hh = (c >> 1) & 1, qq = c & 1;
-        const uint32_t P = hh ? rb[s][i].y : rb[s][i].x, Nm = hh ? rb[s][i].w : rb[s][i].z;
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int sh = 4 * qq + j;
-          const uint32_t pb = (P >> sh) & 0x01010101u, nb = (Nm >> sh) & 0x01010101u;
-          o[j] = expand_flags(pb, nb);
-        }
-        *reinterpret_cast<u32x4*>(&Bs[buf][(c >> 2) * kLd + hh * 32 + qq * 16]) = u32x4{o[0], o[1], o[2], o[3]};
-      }
-    }
-  };
-
-  i32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-
-  // Tile t sits in register slot (t - t0) % S and LDS buffer (t - t0) & 1. Each step
-  // multiplies the staged tile, then stages the next one into the other buffer (the
-  // matrix cores run while the VALU expands weights), refills the freed register slot and
-  // meets the other waves at one barrier.
-  auto compute = [&](int buf) {
-    i32x4 a[FM], b[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      a[i] = *reinterpret_cast<const i32x4*>(&As[buf][(wm * WM + 16 * i + (lane & 15)) * kLd + 16 * (lane >> 4)]);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      b[j] = *reinterpret_cast<const i32x4*>(&Bs[buf][(wn * WN + 16 * j + (lane & 15)) * kLd + 16 * (lane >> 4)]);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-  };
-#pragma unroll
-  for (int s = 0; s < S; ++s) fetch(s, t0 + s);
-  stage(0, 0);
-  fetch(0, t0 + S);
-  __syncthreads();
-  for (int kb = t0; kb < t1; kb += S) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int tk = kb + s;
-      const int ns = (s + 1) % S;
-      if (tk < t1) compute((tk - t0) & 1);
-      if (tk + 1 < t1) stage(ns, (tk + 1 - t0) & 1);
-      fetch(ns, tk + 1 + S);
-      if (tk < t1) __syncthreads();
-    }
-  }
-  __syncthreads();
-
-  // D layout of a 16x16 fragment: lane l holds rows 4*(l/16) + r (r = 0..3), column l % 16.
-  const int nsplit = gridDim.y;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * WM + 16 * i + 4 * (lane >> 4) + r;
-        const int64_t col = n0 + wn * WN + 16 * j + (lane & 15);
-        if (row < M && col < N) {
-          int v = acc[i][j][r];
-          if (nsplit > 1 && !split_arrive(&ws_acc[row * N + col], v, nsplit, &v)) continue;
-          if (acc_out) acc_out[row * N + col] = v;
-          if (y) {
-            const float scale = gamma[row] / 127.0f;
-            y[row * N + col] = static_cast<float>(v) * scale * beta[beta_len == 1 ? 0 : col];
-          }
-        }
-      }
 }
 
 // Register-blocked prefill GEMM. A 256-thread workgroup owns a (4 * 16 FM) x 64 output tile:
@@ -335,35 +184,6 @@ __global__ __launch_bounds__(256) void gemm_rb_kernel(
   }
 }
 
-// Tuning knobs. Only harnesses that compile this file directly change them; the library
-// itself always runs with these defaults.
-int g_gemm_wg_target = 0;      // workgroups the small-M split-K aims for (0: by M)
-int g_gemm_force = -1;         // tile choice override
-
-template <int BM, int BN, int WGM, int S = 4>
-hipError_t launch_tile(const int8_t* q, const float* gamma, int64_t M, int64_t K,
-                       const u32x4* W, const float* beta, int64_t beta_len, int64_t N, float* y,
-                       int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt, hipStream_t s) {
-  const int MT = static_cast<int>((M + BM - 1) / BM), NT = static_cast<int>((N + BN - 1) / BN);
-  const int KT = static_cast<int>(K / 64);
-  const int64_t tiles = static_cast<int64_t>(MT) * NT;
-  int nsplit = 1;
-  if (M <= 64) {   // HBM-bound shapes: fill the chip by splitting K (cheap: M x N atomics)
-    // measured on MI355X: 1024 workgroups suit M <= 16, 512 suit M = 17..64
-    const int64_t target = g_gemm_wg_target ? g_gemm_wg_target : (M <= 16 ? 1024 : 512);
-    nsplit = static_cast<int>(std::min<int64_t>((target + tiles - 1) / tiles, std::max(1, KT / 8)));
-    nsplit = std::max(nsplit, 1);
-  }
-  if (M * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
-  nsplit = std::min(nsplit, kMaxIntSplits);
-  const int tps = (KT + nsplit - 1) / nsplit;
-  nsplit = (KT + tps - 1) / tps;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, S>), dim3(static_cast<unsigned>(tiles), nsplit),
-                     dim3(256), 0, s, q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,
-                     ws_cnt, tps, MT, NT);
-  return hipGetLastError();
-}
-
 // Workgroups the register-blocked kernel aims for before it splits K (0: 256, one per CU).
 int g_gemm_rb_target = 0;
 
@@ -399,34 +219,8 @@ hipError_t launch_rb(const int8_t* q, const float* gamma, int64_t M, int64_t K, 
 
 hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                        const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
-                       float* y, int32_t* acc_out, uint64_t* ws_acc, uint32_t* ws_cnt,
-                       hipStream_t s) {
+                       float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
   const u32x4* W = static_cast<const u32x4*>(wpacked);
-#define BL_TILE(BM_, BN_, WGM_) \
-  launch_tile<BM_, BN_, WGM_>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s)
-#define BL_TILES(BM_, BN_, WGM_, S_) \
-  launch_tile<BM_, BN_, WGM_, S_>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, ws_cnt, s)
-  switch (g_gemm_force) {
-    case 0: return BL_TILE(16, 128, 1);
-    case 1: return BL_TILE(32, 128, 2);
-    case 2: return BL_TILE(64, 128, 2);
-    case 3: return BL_TILE(128, 128, 2);
-    case 4: return BL_TILE(128, 64, 4);
-    case 5: return BL_TILE(64, 64, 2);
-    case 6: return BL_TILE(16, 256, 1);
-    case 7: return BL_TILE(64, 256, 2);
-    case 8: return BL_TILE(128, 256, 2);
-    case 9: return BL_TILE(256, 128, 2);
-    case 10: return BL_TILES(64, 64, 2, 8);
-    case 11: return BL_TILES(128, 128, 2, 8);
-    case 12: return BL_TILES(64, 128, 2, 8);
-    case 13: return BL_TILES(16, 128, 1, 8);
-    case 14: return BL_TILES(32, 128, 2, 8);
-    case 15: return BL_TILES(64, 64, 2, 2);
-    case 16: return BL_TILE(64, 64, 2);
-    case 17: return launch_rb<2>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, s);
-    default: break;
-  }
   // Batched decode: weights streamed into registers and expanded there (tern_mfma.hip);
   // measured 1.1-2.2x faster than LDS tiles for M <= 64 on the 70B-shaped linears.
   if (M <= 64) return launch_tern_mfma(q, gamma, M, K, wpacked, beta, beta_len, N, y, acc_out, ws_acc, s);
@@ -436,9 +230,6 @@ hipError_t launch_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K
   // register tiles, 128 x 64 and 256 x 64, were slower: too few waves per SIMD to hide the
   // per-k-tile latencies).
   return launch_rb<1>(q, gamma, M, K, W, beta, beta_len, N, y, acc_out, ws_acc, s);
-#undef BL_TILE
-#undef BL_TILES
 }
-
 
 }  // namespace bl
