@@ -49,10 +49,12 @@
  *  T2-MF64 (ternary, for the int8 matrix cores). N % 64 == 0, K % 64 == 0. Tiles as
  *    T2-PN-64 (same order and size), read as 256 uint32 words. Tile row r = 16f + u
  *    (f = 0..3, u = 0..15) and tile input c = 16g + 4j + i (g, j, i = 0..3) sit in word
- *    4*(16g + u) + f at bits 8i + 2j .. 8i + 2j + 1, holding the code w + 1 (0, 1, 2;
- *    3 is invalid). N*K/4 bytes. (Lane 16g + u of a wave loads the 16 bytes at
- *    16*(16g + u): exactly the weights of its four matrix-core fragments, and
- *    (word >> 2j) & 0x03030303 is one int8 operand dword of codes.)
+ *    4*(16g + u) + j at bits 8i + 2f .. 8i + 2f + 1. For f = 0, 1, 2 the field holds
+ *    w + 1 (0, 1, 2; 3 is invalid), for f = 3 w in two's complement (00, 01, 11 for
+ *    0, +1, -1; 10 is invalid). N*K/4 bytes. (Lane 16g + u of a wave loads the 16 bytes
+ *    at 16*(16g + u): exactly the weights of its four matrix-core fragments, and
+ *    word j & (0x03030303 << 2f) is one int8 operand dword of fragment f: bytes
+ *    4^f (w + 1) for f < 3, signed bytes 64 w for f = 3.)
  *  S1-128 (sign). N % 64 == 0, K % 128 == 0. Tile (tn, tk) = rows 64tn..+63, inputs
  *    128tk..+127, 1024 bytes at byte (tn*(K/128) + tk)*1024, read as 256 uint32 words.
  *    Tile row r = 16f + u (f = 0..3, u = 0..15) and tile input c = 32s + 8g + 2q + e
@@ -182,8 +184,9 @@ int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
 
 /* Batched product from T2-MF64 weights on int8 matrix cores ([b158] "实验及结果": batched
  * serving; Fig. 3: int8 accumulation), built for batched decode (M <= 64, any M accepted).
- * The matrix cores multiply q by the codes w + 1; the final sum subtracts rowsum[m], which
- * must be sum_k q[m,k] (bl_quant_act_int8 computes it), so
+ * The matrix cores multiply q by the scaled fields of the layout; for outputs in the first
+ * 48 rows of each 64-row band the final sum subtracts rowsum[m], which must be
+ * sum_k q[m,k] (bl_quant_act_int8 computes it), so
  *   acc[m,n] = sum_k w[n,k] q[m,k]   exactly (int32), and
  *   y[m,n] = acc[m,n] * (gamma[m] / 127) * beta[beta_len == 1 ? 0 : n].
  * q int8 [M, K] (16-byte aligned rows), rowsum int32 [M], wmf T2-MF64 [N, K]. Outputs: y fp32

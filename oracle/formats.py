@@ -23,8 +23,11 @@ X8-64 (activation bit planes of int8 q, used by the add-only GEMV).
 T2-MF64 (ternary, 2 bits/weight, for int8 matrix-core operands). N % 64 == 0,
   K % 64 == 0. Tiles as T2-PN-64 (64 rows x 64 inputs, 1024 bytes, same order), read
   as 256 little-endian uint32 words. Tile row r = 16f + u (f, u: 0..3, 0..15) and tile
-  input c = 16g + 4j + i (g, j, i: 0..3) sit in word 4*(16g + u) + f at bits 8i + 2j
-  and 8i + 2j + 1, holding the code w + 1 (0, 1, 2; 3 is invalid).
+  input c = 16g + 4j + i (g, j, i: 0..3) sit in word 4*(16g + u) + j at bits 8i + 2f
+  and 8i + 2f + 1. For f = 0, 1, 2 the field holds the code w + 1 (0, 1, 2; 3 is
+  invalid); for f = 3 it holds w in two's complement (00 = 0, 01 = +1, 11 = -1; 10 is
+  invalid). Masking word j with 0x03030303 << 2f leaves, in byte i, 4^f (w + 1) for
+  f < 3 and, read as a signed byte, 64 w for f = 3.
 
 S1-128 (sign, 1 bit/weight). N % 64 == 0, K % 128 == 0.
   Tile (tn, tk) = rows 64tn.., inputs 128tk.., 1024 bytes at byte
@@ -97,48 +100,51 @@ def unpack_ternary(packed: np.ndarray, N: int, K: int, count_invalid: bool = Fal
 
 
 def _mf_byte_and_shift(N: int, K: int):
-    """Byte offset of the 2-bit code of every (n, k) and its shift within that byte,
-    straight from the T2-MF64 text."""
+    """Byte offset of the 2-bit field of every (n, k), its shift within that byte and its
+    fragment f (which fixes the field's encoding), straight from the T2-MF64 text."""
     n = np.arange(N, dtype=np.int64)[:, None]
     k = np.arange(K, dtype=np.int64)[None, :]
     tn, r = n // 64, n % 64
     tk, c = k // 64, k % 64
     f, u = r // 16, r % 16
     g, j, i = c // 16, (c // 4) % 4, c % 4
-    word = 4 * (16 * g + u) + f
-    wbit = 8 * i + 2 * j
+    word = 4 * (16 * g + u) + j
+    wbit = 8 * i + 2 * f
     byte = (tn * (K // 64) + tk) * 1024 + 4 * word + wbit // 8
-    return byte, np.broadcast_to(wbit % 8, byte.shape)
+    return byte, np.broadcast_to(wbit % 8, byte.shape), np.broadcast_to(f, byte.shape)
 
 
 def pack_ternary_mf(codes: np.ndarray, count_invalid: bool = False):
-    """int8 codes [N, K] -> uint8 T2-MF64 bytes [N*K/4]: code w + 1 per weight.
+    """int8 codes [N, K] -> uint8 T2-MF64 bytes [N*K/4]: field w + 1 (rows 16f + u of a
+    tile with f < 3) or w in two's complement (f = 3).
 
-    A code other than -1/0/+1 packs as 0 (code 1) and is counted as invalid.
-    Parity: pinned by hand-worked bytes, the round trip and agreement with T2-PN-64 in
-    the CPU tests."""
+    A code other than -1/0/+1 packs as w = 0 and is counted as invalid.
+    Parity: pinned by hand-worked bytes, the round trip, agreement with T2-PN-64 and the
+    operand identity in the CPU tests."""
     codes = np.asarray(codes)
     N, K = codes.shape
     assert N % 64 == 0 and K % 64 == 0, "T2-MF64 needs N % 64 == 0 and K % 64 == 0"
     valid = (codes == 1) | (codes == 0) | (codes == -1)
-    c = np.where(valid, codes.astype(np.int64) + 1, 1)
+    w = np.where(valid, codes.astype(np.int64), 0)
+    byte, shift, f = _mf_byte_and_shift(N, K)
+    field = np.where(f < 3, w + 1, w & 3)
     out = np.zeros(ternary_packed_bytes(N, K), dtype=np.uint8)
-    byte, shift = _mf_byte_and_shift(N, K)
-    np.bitwise_or.at(out, byte.ravel(), (c << shift).astype(np.uint8).ravel())
+    np.bitwise_or.at(out, byte.ravel(), (field << shift).astype(np.uint8).ravel())
     if count_invalid:
         return out, int(np.count_nonzero(~valid))
     return out
 
 
 def unpack_ternary_mf(packed: np.ndarray, N: int, K: int, count_invalid: bool = False):
-    """T2-MF64 bytes -> int8 codes [N, K]. Code 3 decodes to 0 and is counted invalid."""
+    """T2-MF64 bytes -> int8 codes [N, K]. An invalid field (3 for f < 3, 2 for f = 3)
+    decodes to 0 and is counted."""
     packed = np.asarray(packed, dtype=np.uint8).ravel()
     assert packed.size == ternary_packed_bytes(N, K)
-    byte, shift = _mf_byte_and_shift(N, K)
-    c = (packed[byte] >> shift.astype(np.uint8)) & 3
-    bad = c == 3
-    codes = c.astype(np.int8) - 1
-    codes[bad] = 0
+    byte, shift, f = _mf_byte_and_shift(N, K)
+    c = ((packed[byte] >> shift.astype(np.uint8)) & 3).astype(np.int64)
+    bad = np.where(f < 3, c == 3, c == 2)
+    w = np.where(f < 3, c - 1, np.where(c == 3, -1, c))
+    codes = np.where(bad, 0, w).astype(np.int8)
     if count_invalid:
         return codes, int(np.count_nonzero(bad))
     return codes

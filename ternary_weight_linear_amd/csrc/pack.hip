@@ -86,9 +86,9 @@ __global__ void unpack_ternary_kernel(const uint4* __restrict__ in, int64_t N, i
 // float W [N, K] -> S1-128. Thread i <-> one 16-byte record: tile i / 64, record L = i % 64
 // = 16g + u, holding word f (rows 16f + u) with the signs of tile inputs 32s + 8g + j,
 // j = 2q + e, at bit 16e + 4s + q.
-// T2-MF64: one thread per 16-byte record of a tile (record 16g + u = word f of rows
-// 16f + u, inputs 16g .. 16g + 15 of the tile); code w + 1 of input 16g + 4j + i at bits
-// 8i + 2j. Invalid codes pack as code 1 (w = 0) and are counted.
+// T2-MF64: one thread per 16-byte record of a tile (record 16g + u: word j holds, at bits
+// 8i + 2f, the field of row 16f + u, input 16g + 4j + i of the tile: w + 1 for f < 3, w in
+// two's complement for f = 3). Invalid codes pack as w = 0 and are counted.
 __global__ void pack_ternary_mf_kernel(const int8_t* __restrict__ codes, int64_t N, int64_t K,
                                        uint4* __restrict__ out, int32_t* n_invalid) {
   const int64_t KT = K / 64;
@@ -97,33 +97,34 @@ __global__ void pack_ternary_mf_kernel(const int8_t* __restrict__ codes, int64_t
   const int64_t tile = idx >> 6;
   const int rec = static_cast<int>(idx & 63), g = rec >> 4, u = rec & 15;
   const int64_t tn = tile / KT, tk = tile % KT;
-  uint32_t word[4];
+  uint32_t word[4] = {0, 0, 0, 0};
   int bad = 0;
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const int64_t n = tn * 64 + 16 * f + u;
     const uint4 v = *reinterpret_cast<const uint4*>(codes + n * K + tk * 64 + 16 * g);
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};   // w4[j] byte i = code of input 16g + 4j + i
-    uint32_t wd = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int8_t c = static_cast<int8_t>((w4[j] >> (8 * i)) & 0xFF);
-        uint32_t code = 1;
-        if (c == 1 || c == 0 || c == -1) code = static_cast<uint32_t>(c + 1);
-        else ++bad;
-        wd |= code << (8 * i + 2 * j);
+        int c = static_cast<int8_t>((w4[j] >> (8 * i)) & 0xFF);
+        if (c != 1 && c != 0 && c != -1) {
+          c = 0;
+          ++bad;
+        }
+        const uint32_t field = f < 3 ? static_cast<uint32_t>(c + 1) : static_cast<uint32_t>(c) & 3u;
+        word[j] |= field << (8 * i + 2 * f);
       }
-    word[f] = wd;
   }
   out[idx] = make_uint4(word[0], word[1], word[2], word[3]);
   if (bad && n_invalid) atomicAdd(n_invalid, bad);
 }
 
 // T2-PN-64 -> T2-MF64, one thread per output record. Input 16g + 4j + i of a tile row is
-// bit 8i + 4(g % 2) + j of half g / 2 of the row's P and N words; code = 1 + p - n per byte
-// (no byte ever borrows: 1 + p >= n). A (P, N) = (1, 1) pair becomes code 1 and is counted.
+// bit 8i + 4(g % 2) + j of half g / 2 of the row's P and N words. Per byte the field is
+// 1 + p - n for f < 3 (no byte ever borrows: 1 + p >= n) and p | 3n for f = 3 (01 / 11).
+// A (P, N) = (1, 1) pair becomes w = 0 and is counted.
 __global__ void repack_pn_to_mf_kernel(const uint4* __restrict__ in, int64_t N, int64_t K,
                                        uint4* __restrict__ out, int32_t* n_invalid) {
   const int64_t KT = K / 64;
@@ -131,22 +132,22 @@ __global__ void repack_pn_to_mf_kernel(const uint4* __restrict__ in, int64_t N, 
   if (idx >= N * KT) return;
   const int64_t tile = idx >> 6;
   const int rec = static_cast<int>(idx & 63), g = rec >> 4, u = rec & 15;
-  uint32_t word[4];
+  uint32_t word[4] = {0, 0, 0, 0};
   int bad = 0;
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const uint4 row = in[tile * 64 + 16 * f + u];
     const uint32_t P = (g >> 1) ? row.y : row.x, Nm = (g >> 1) ? row.w : row.z;
-    uint32_t wd = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int sh = 4 * (g & 1) + j;
       const uint32_t pb = (P >> sh) & 0x01010101u, nb = (Nm >> sh) & 0x01010101u;
       const uint32_t both = pb & nb;
       bad += __builtin_popcount(both);
-      wd |= ((0x01010101u + (pb ^ both)) - (nb ^ both)) << (2 * j);
+      const uint32_t p = pb ^ both, n = nb ^ both;
+      const uint32_t field = f < 3 ? (0x01010101u + p) - n : p | (n * 3u);
+      word[j] |= field << (2 * f);
     }
-    word[f] = wd;
   }
   out[idx] = make_uint4(word[0], word[1], word[2], word[3]);
   if (bad && n_invalid) atomicAdd(n_invalid, bad);

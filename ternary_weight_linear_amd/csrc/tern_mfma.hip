@@ -78,7 +78,8 @@ __device__ __forceinline__ void tern_load(TernTile<FM>& T, const TernArgs& a, in
 // Epilogue shared by both kernels (wave 0, after the LDS reduction): per 16-row tile fm,
 // the 16 outputs of this lane meet the other K splits with all 16 adds in flight at once
 // (split_arrive_batch; one round trip measured faster here than two batches of 8 with
-// fewer registers), then rowsum (T2-MF64 only) is subtracted and y / acc written.
+// fewer registers), and y / acc are written. T2-MF64 (rowsum given): fragment f's sums are
+// shifted right by 2f first, and rowsum is taken away from fragments f < 3.
 // D layout: lane l holds rows 4*(l/16) + i of the q tile, column l % 16 of fragment f.
 template <int FM>
 __device__ __forceinline__ void tern_epilogue(const TernArgs& a, const i32x4 (&acc)[FM][4],
@@ -95,6 +96,7 @@ __device__ __forceinline__ void tern_epilogue(const TernArgs& a, const i32x4 (&a
     for (int k = 0; k < 16; ++k) {
       const int f = k / 4, i = k % 4, e = (fm * 4 + f) * 4 + i;
       v[k] = acc[fm][f][i] + red[0][e][lane] + red[1][e][lane] + red[2][e][lane];
+      if (rowsum) v[k] >>= 2 * f;   // exact: a multiple of 4^f
       if (m0 + 16 * fm + 4 * g + i < a.M) active |= 1u << k;
     }
     auto word = [&](int k) __attribute__((always_inline)) {
@@ -108,7 +110,7 @@ __device__ __forceinline__ void tern_epilogue(const TernArgs& a, const i32x4 (&a
       const int64_t row = m0 + 16 * fm + 4 * g + k % 4;
       const int64_t col = band * 64 + 16 * (k / 4) + u;
       int r = v[k];
-      if (rowsum) r -= rowsum[row];
+      if (rowsum && k / 4 < 3) r -= rowsum[row];
       if (a.acc_out) a.acc_out[row * a.N + col] = r;
       if (a.y)
         a.y[row * a.N + col] = static_cast<float>(r) * (a.gamma[row] / 127.0f) *
@@ -227,13 +229,17 @@ __global__ __launch_bounds__(256) void tern_mfma_kernel(const TernArgs a) {
 
 // ---- T2-MF64 weights -------------------------------------------------------------------
 // The second ternary layout stores, for each lane 16g + u of a wave, the 16 bytes its four
-// fragments need: word f holds codes w + 1 of weight row 16f + u, inputs 16g + 4j + i at
-// bits 8i + 2j. So a tile costs one 16-byte load per lane (no lane loads bytes another
-// lane also loads), (word >> 2j) & 0x03030303 is one operand dword (seven ALU ops per
-// fragment) and one MFMA per fragment multiplies q by w + 1. The final writer subtracts
-// sum_k q[m, k] (from the quantiser), which makes the integers those of q . w exactly.
-// A split's partial |sum q (w + 1)| <= 254 * 64 * tiles stays below the split words' 2^23
-// bias as long as a split spans at most kMfMaxSplitTiles tiles.
+// fragments need: word j holds, at bits 8i + 2f, the field of weight row 16f + u, input
+// 16g + 4j + i (w + 1 for f < 3, w in two's complement for f = 3). So a tile costs one
+// 16-byte load per lane (no lane loads bytes another lane also loads) and fragment f's
+// operand dword j is one AND, word j & (0x03030303 << 2f): bytes 4^f (w + 1) for f < 3 and,
+// as signed bytes, 64 w for f = 3 (four ALU ops per fragment). One MFMA per fragment then
+// accumulates 4^f sum q (w + 1), resp. 64 sum q w; shifting right by 2f is exact, and for
+// f < 3 the final writer takes away sum_k q[m, k] (from the quantiser), which makes the
+// integers those of q . w exactly. A split's shifted partial |sum q (w + 1)| <= 254 * 64 *
+// tiles stays below the split words' 2^23 bias as long as a split spans at most
+// kMfMaxSplitTiles tiles; unshifted, 16 * 254 * K and 64 * 127 * K stay below 2^31 for
+// K <= 65536.
 #ifndef BL_MF_DEPTH
 #define BL_MF_DEPTH 3
 #endif
@@ -262,7 +268,7 @@ __device__ __forceinline__ void mf_compute(const MfTile<FM>& T, i32x4 (&acc)[FM]
   for (int f = 0; f < 4; ++f) {
     i32x4 b;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = static_cast<int>((w4[f] >> (2 * j)) & 0x03030303u);
+    for (int j = 0; j < 4; ++j) b[j] = static_cast<int>(w4[j] & (0x03030303u << (2 * f)));
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
       acc[fm][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, T.a[fm]), b,
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
 // A workgroup of four waves owns four consecutive bands (one per wave), 16 FM rows of q
 // (FM = 1 or 2; more rows take more workgroups) and a K range. For each chunk of kQC tiles the
 // workgroup copies q[rows, chunk] into LDS once; each wave decodes its own weight tile once
-// (28 ALU ops) and runs FM x 4 MFMAs with A fragments read from LDS, so neither the q bytes
+// (16 ALU ops) and runs FM x 4 MFMAs with A fragments read from LDS, so neither the q bytes
 // nor the decoding are repeated per 16 rows. Weights come through a buffer resource over
 // the wave's band and K range: past the range a load returns zero without a memory access,
 // and a zero code adds nothing to sum q (w + 1), so the ring of R chunks is refilled
@@ -432,7 +438,7 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[f][j] = static_cast<int>((w4[f] >> (2 * j)) & 0x03030303u);
+        for (int j = 0; j < 4; ++j) b[f][j] = static_cast<int>(w4[j] & (0x03030303u << (2 * f)));
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const i32x4 av = *reinterpret_cast<const i32x4*>(
@@ -482,12 +488,13 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
     for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
       for (int k = 0; k < 16; ++k)   // output k: row 4g + k % 4, column 16 (k / 4) + u
-        st[(4 * g + k % 4) * kStRow + 16 * (k / 4) + u] = acc[fm][k / 4][k % 4];
+        st[(4 * g + k % 4) * kStRow + 16 * (k / 4) + u] = acc[fm][k / 4][k % 4] >> (2 * (k / 4));
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = 16 * fm + r;
-        const int v = st[r * kStRow + lane] - __builtin_amdgcn_readlane(rs_l, rr);
+        const int rsv = __builtin_amdgcn_readlane(rs_l, rr);
+        const int v = st[r * kStRow + lane] - (lane < 48 ? rsv : 0);   // fragments f < 3
         const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs_l), rr));
         const int64_t row = m0 + rr;
         if (active && row < a.M) {
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
     uint32_t live = 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      v[k] = acc[fm][k / 4][k % 4];
+      v[k] = acc[fm][k / 4][k % 4] >> (2 * (k / 4));
       if (m0 + 16 * fm + 4 * g + k % 4 < a.M) live |= 1u << k;
     }
     auto word = [&](int k) __attribute__((always_inline)) {
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
       if (!((done >> k) & 1u)) continue;
       const int64_t row = m0 + 16 * fm + 4 * g + k % 4;
       const int64_t col = band * 64 + 16 * (k / 4) + u;
-      const int r = v[k] - rowsum[row];
+      const int r = v[k] - (k / 4 < 3 ? rowsum[row] : 0);
       if (a.acc_out) a.acc_out[row * a.N + col] = r;
       if (a.y)
         a.y[row * a.N + col] = static_cast<float>(r) * (a.gamma[row] / 127.0f) *

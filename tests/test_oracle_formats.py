@@ -70,24 +70,34 @@ def test_t2_invalid_codes():
 
 
 # ----------------------------------------------------------------------------- T2-MF64
-# Hand-worked from the layout text on a 128 x 128 matrix whose other codes are -1 (code 0,
-# all bits clear): row r = 16f + u, input c = 16g + 4j + i -> word 4(16g + u) + f, bits
-# 8i + 2j (byte i of the word, shift 2j), value w + 1.
+# Hand-worked from the layout text on a 128 x 128 matrix whose other weights make every
+# field zero (-1 in rows 16f + u with f < 3, field w + 1 = 0; 0 in rows with f = 3, field
+# w = 0): row r = 16f + u, input c = 16g + 4j + i -> word 4(16g + u) + j, byte i of the
+# word, shift 2f; the field is w + 1 for f < 3 and w in two's complement for f = 3.
+def _mf_background():
+    codes = np.full((128, 128), -1, dtype=np.int8)
+    codes[(np.arange(128) % 64) >= 48, :] = 0
+    return codes
+
+
 @pytest.mark.parametrize("n,k,code,byte,value", [
-    (0, 0, 1, 0, 0x02),          # word 0, byte 0, shift 0, code 2
-    (0, 1, 0, 1, 0x01),          # i = 1 -> byte 1, code 1
-    (0, 4, 1, 0, 0x08),          # j = 1 -> shift 2
-    (0, 15, 1, 3, 0x80),         # i = 3, j = 3 -> byte 3, shift 6
+    (0, 0, 1, 0, 0x02),          # word 0, byte 0, shift 0, field 2
+    (0, 1, 0, 1, 0x01),          # i = 1 -> byte 1, field 1
+    (0, 4, 1, 4, 0x02),          # j = 1 -> word 1
+    (0, 15, 1, 15, 0x02),        # j = 3, i = 3 -> word 3, byte 3
     (0, 16, 0, 256, 0x01),       # g = 1 -> word 64
     (1, 0, 1, 16, 0x02),         # u = 1 -> word 4
-    (16, 0, 0, 4, 0x01),         # f = 1 -> word 1
-    (63, 63, 1, 1023, 0x80),     # word 255, byte 3, shift 6
+    (16, 0, 0, 0, 0x04),         # f = 1 -> shift 2, field 1
+    (32, 0, 1, 0, 0x20),         # f = 2 -> shift 4, field 2
+    (48, 0, 1, 0, 0x40),         # f = 3 -> shift 6, field 01 (w = +1)
+    (48, 0, -1, 0, 0xC0),        # f = 3, field 11 (w = -1)
+    (63, 63, -1, 1023, 0xC0),    # u = 15, g = 3, j = 3, i = 3: word 255, byte 3
     (0, 64, 1, 1024, 0x02),      # second k tile
     (64, 0, 0, 2048, 0x01),      # second row band: tile (1, 0)
-    (127, 127, 0, 4095, 0x40),   # tile (1, 1), word 255, byte 3, shift 6, code 1
+    (127, 127, 1, 4095, 0x40),   # tile (1, 1), word 255, byte 3, f = 3
 ])
 def test_mf_worked_bytes(n, k, code, byte, value):
-    codes = np.full((128, 128), -1, dtype=np.int8)
+    codes = _mf_background()
     codes[n, k] = code
     packed = oracle.pack_ternary_mf(codes)
     expect = np.zeros_like(packed)
@@ -97,10 +107,11 @@ def test_mf_worked_bytes(n, k, code, byte, value):
 
 def test_mf_layout_is_a_bijection():
     from oracle.formats import _mf_byte_and_shift
-    byte, shift = _mf_byte_and_shift(128, 192)
+    byte, shift, f = _mf_byte_and_shift(128, 192)
     slots = byte.astype(np.int64) * 8 + shift
     assert np.unique(slots).size == 128 * 192
     assert slots.min() == 0 and byte.max() == 128 * 192 // 4 - 1 and np.all(shift % 2 == 0)
+    assert np.array_equal(shift, 2 * f)
 
 
 def test_mf_round_trip_and_agreement_with_t2():
@@ -110,37 +121,63 @@ def test_mf_round_trip_and_agreement_with_t2():
     assert np.array_equal(oracle.unpack_ternary_mf(mf, 192, 320), codes)
     pn = oracle.pack_ternary(codes)
     assert np.array_equal(oracle.unpack_ternary(pn, 192, 320), oracle.unpack_ternary_mf(mf, 192, 320))
-    # no word holds the invalid code 3
+    # no field holds an invalid value (3 at shifts 0, 2, 4; 2 at shift 6)
     w = _words(mf)
     for s in range(0, 32, 2):
-        assert not np.any(((w >> s) & 3) == 3)
+        fld = (w >> s) & 3
+        assert not np.any(fld == (2 if s % 8 == 6 else 3))
 
 
 def test_mf_operand_extraction():
-    """The use the layout is cut for: in record 16g + u of a tile, (word f >> 2j) &
-    0x03030303 holds, in byte i, w + 1 of row 16f + u, input 16g + 4j + i."""
+    """The use the layout is cut for: in record 16g + u of a tile, word j masked with
+    0x03030303 << 2f holds, in byte i, 4^f (w + 1) (f < 3) or, as a signed byte, 64 w
+    (f = 3), for w of row 16f + u, input 16g + 4j + i."""
     codes = synth.ternary_codes(synth.matrix_key(0, 99, 2, 0), 64, 64)
-    w = _words(oracle.pack_ternary_mf(codes)).reshape(64, 4)     # [record, f]
+    w = _words(oracle.pack_ternary_mf(codes)).reshape(64, 4)     # [record, j]
     for g in range(4):
         for u in range(16):
             for f in range(4):
                 for j in range(4):
-                    d = (int(w[16 * g + u, f]) >> (2 * j)) & 0x03030303
-                    got = [(d >> (8 * i)) & 0xFF for i in range(4)]
-                    want = [int(codes[16 * f + u, 16 * g + 4 * j + i]) + 1 for i in range(4)]
+                    d = int(w[16 * g + u, j]) & (0x03030303 << (2 * f))
+                    got = [int(np.int8(np.uint8((d >> (8 * i)) & 0xFF))) for i in range(4)]
+                    wt = [int(codes[16 * f + u, 16 * g + 4 * j + i]) for i in range(4)]
+                    want = [(4 ** f) * (x + 1) for x in wt] if f < 3 else [64 * x for x in wt]
                     assert got == want
+
+
+def test_mf_operand_dot_identity():
+    """Summing q times the masked bytes over a tile row, shifting right by 2f and taking
+    away sum q for f < 3 gives sum q w exactly (what the kernels' epilogues do)."""
+    rng = np.random.default_rng(5)
+    codes = synth.ternary_codes(synth.matrix_key(0, 99, 3, 0), 64, 64)
+    q = rng.integers(-127, 128, size=64)
+    w = _words(oracle.pack_ternary_mf(codes)).reshape(64, 4)
+    for f in range(4):
+        for u in range(16):
+            s = 0
+            for g in range(4):
+                for j in range(4):
+                    d = int(w[16 * g + u, j]) & (0x03030303 << (2 * f))
+                    for i in range(4):
+                        s += int(q[16 * g + 4 * j + i]) * int(np.int8(np.uint8((d >> (8 * i)) & 0xFF)))
+            assert s % (4 ** f) == 0
+            v = (s >> (2 * f)) - (int(q.sum()) if f < 3 else 0)
+            assert v == int(np.dot(q, codes[16 * f + u].astype(np.int64)))
 
 
 def test_mf_invalid_codes():
     codes = np.zeros((64, 64), dtype=np.int8)
     codes[0, :3] = [2, -5, -1]
+    codes[48, :3] = [3, 1, -1]
     packed, bad = oracle.pack_ternary_mf(codes, count_invalid=True)
-    assert bad == 2
-    assert list(oracle.unpack_ternary_mf(packed, 64, 64)[0, :3]) == [0, 0, -1]
+    assert bad == 3
+    back = oracle.unpack_ternary_mf(packed, 64, 64)
+    assert list(back[0, :3]) == [0, 0, -1] and list(back[48, :3]) == [0, 1, -1]
     packed = packed.copy()
-    packed[0] |= 0x03                                  # code 3 at (0, 0)
+    packed[0] |= 0x03                                  # field 3 at (0, 0): f = 0
+    packed[0] = (packed[0] & 0x3F) | 0x80              # field 10 at (48, 0): f = 3
     back, bad2 = oracle.unpack_ternary_mf(packed, 64, 64, count_invalid=True)
-    assert bad2 == 1 and back[0, 0] == 0
+    assert bad2 == 2 and back[0, 0] == 0 and back[48, 0] == 0
 
 
 # ----------------------------------------------------------------------------- S1-128
