@@ -173,8 +173,8 @@ def repack_stack_mf(torch, tw, dev, layers):
 
 
 def decode_pass_mf(torch, tw, synth, dev, layers_mf, M):
-    """Batched decode over T2-MF64 weights: per group one bl_bitlinear_forward_mf call
-    (quantiser + matrix-core product; same activations as decode_pass)."""
+    """Decode over T2-MF64 weights: per group one bl_bitlinear_forward_mf call (M <= 16: one
+    fused launch; above: quantiser + matrix-core product; same activations as decode_pass)."""
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=dev)
     items = []
     for li, lg in enumerate(layers_mf):
@@ -197,7 +197,7 @@ def decode_pass_mf(torch, tw, synth, dev, layers_mf, M):
 
     algo_bytes = sum(it["w"].numel() + 2 * M * it["K"] + 4 * M * it["N"] for it in items)
     weight_bytes = sum(it["w"].numel() for it in items)
-    return items, full_pass, algo_bytes, weight_bytes, 2 * len(items)
+    return items, full_pass, algo_bytes, weight_bytes, (1 if M <= 16 else 2) * len(items)
 
 
 def bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, steps, warmup):

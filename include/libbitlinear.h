@@ -197,9 +197,11 @@ int bl_bitlinear_gemm_mf(const int8_t* q, const float* gamma, const int32_t* row
                          int64_t N, float* y, int32_t* acc, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* The whole b1.58 linear from fp16 activations and T2-MF64 weights: quantise (q, gamma and
- * rowsum into ws), then bl_bitlinear_gemm_mf. Same result as bl_bitlinear_forward on the
- * same weights in T2-PN-64. x fp16 [M, K]; K <= 28672. Uses ws (bl_workspace_bytes(M, N, K)). */
+/* The whole b1.58 linear from fp16 activations and T2-MF64 weights. M <= 16 (decode): one
+ * launch computes gamma, quantises into LDS and multiplies on the int8 matrix cores;
+ * M > 16: quantise (q, gamma and rowsum into ws), then bl_bitlinear_gemm_mf. Same result as
+ * bl_bitlinear_forward on the same weights in T2-PN-64. x fp16 [M, K]; K <= 28672. Uses ws
+ * (bl_workspace_bytes(M, N, K)). */
 int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void* wmf,
                             const float* beta, int64_t beta_len, int64_t N, float* y, void* ws,
                             size_t ws_bytes, void* stream);

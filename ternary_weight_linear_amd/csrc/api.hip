@@ -332,10 +332,15 @@ int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void*
       overlap(y, yb, beta, beta_len * 4) || overlap(y, yb, ws, ws_bytes))
     return BL_ERR_ALIAS;
   char* w = static_cast<char*>(ws);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // decode: one launch quantises and multiplies (the weights are read once for M <= 16)
+  if (mf_decode_fits(M, N, K))
+    return check_launch(launch_mf_decode(x, static_cast<int>(M), K, wmf, beta, beta_len, N, y,
+                                         reinterpret_cast<uint64_t*>(w + L.acc_off), s),
+                        "bl_bitlinear_forward_mf");
   auto* qbuf = reinterpret_cast<int8_t*>(w + L.q_off);
   auto* gbuf = reinterpret_cast<float*>(w + L.gamma_off);
   auto* rbuf = reinterpret_cast<int32_t*>(w + L.rowsum_off);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_quant_act(x, M, K, qbuf, gbuf, rbuf, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward_mf (quantise)");
   return check_launch(launch_tern_mf(qbuf, gbuf, rbuf, M, K, wmf, beta, beta_len, N, y, nullptr,

@@ -109,6 +109,12 @@ hipError_t stack_read_status(const void* plan, uint32_t* status, hipStream_t s);
 hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s);
+// Fused quantise + product from T2-MF64 weights for M <= 16 (K <= 32768) where
+// mf_decode_fits (a workgroup's K range must fit in LDS).
+bool mf_decode_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mf_decode(const uint16_t* x, int M, int64_t K, const void* wmf,
+                            const float* beta, int64_t beta_len, int64_t N, float* y,
+                            uint64_t* ws_acc, hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);
@@ -133,6 +139,20 @@ __device__ __forceinline__ int quant_q(float a, float g, float rg) {
     d = near ? e : d;
   }
   return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d), -127.0f, 127.0f));
+}
+
+// Maximum over the 64 lanes of a wave, returned to every lane: DPP steps within quads,
+// half rows and rows, then the row broadcasts (lane 15 -> row 1 and 3, lane 31 -> rows 2
+// and 3), leaving the maximum in lane 63. Lanes a step does not write keep their own value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto step = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x142, 0xA, 0xF, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x143, 0xC, 0xF, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 // popcount(x) + acc in one v_bcnt_u32_b32 (its second operand accumulates). Written out:

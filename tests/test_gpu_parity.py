@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import synth
+import synth.gpu as sgpu
 import ternary_weight_linear_amd as tw
 from tests.gpu_util import DEV, assert_rel, assert_scaled, dev, host, say
 
@@ -691,6 +692,86 @@ def test_gemm_mf_acc_and_output(M, N, K):
     assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, beta))
     y2, _ = tw.bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, dev(np.array([beta])), N)
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+# Decode through T2-MF64 (M <= 16: one fused launch). Shapes: one tile; ragged band groups
+# (inactive waves) with long rows (row loads past 8192 inputs); the largest K; several
+# chunks per workgroup (K split in two over wide outputs); no K split at all (>= 512 band
+# groups); every row-tile width 1, 2, 4, 8, 16 with unused rows.
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 320, 8256), (2, 128, 28672),
+                                   (1, 65536, 16384), (3, 65536, 16384), (8, 65536, 8192),
+                                   (16, 65536, 8192), (1, 131072, 256), (5, 448, 4160),
+                                   (13, 192, 2048), (4, 10240, 8192)])
+def test_forward_mf_decode_equals_forward(M, N, K):
+    """The fused decode kernel gives the outputs of the unfused T2-PN-64 path to the bit and
+    matches the oracle on sampled rows."""
+    say("forward mf decode", M, N, K)
+    x = synth.normal_fp16((M, K), 0, 135, M, K)
+    key = synth.matrix_key(0, 136, N, K)
+    codes_d = sgpu.ternary_codes(key, N, K, DEV)     # the GPU twin of synth.ternary_codes
+    beta = np.float32(0.0173)
+    packed = tw.bl_pack_ternary(codes_d)
+    wmf = tw.bl_pack_ternary_mf(codes_d)
+    del codes_d
+    b = dev(np.array([beta], np.float32))
+    y_pn = tw.bl_bitlinear_forward(dev(x), packed, b, N, path=tw.BL_PATH_GEMM)
+    y_mf = tw.bl_bitlinear_forward_mf(dev(x), wmf, b, N)
+    assert np.array_equal(host(y_pn).view(np.uint32), host(y_mf).view(np.uint32))
+    rows = np.unique(np.linspace(0, N - 1, 97).astype(np.int64))
+    yref, _, _, _ = oracle.bitlinear_forward(x, synth.ternary_codes(key, N, K, rows=rows), beta)
+    assert_rel(host(y_mf)[:, rows], yref)
+
+
+def _mf_q(x, wmf_eye, K):
+    """The fused T2-MF64 decode kernel over an identity weight matrix with beta = 1: y = q *
+    fp32(gamma / 127) up to one rounding; recover q (exact: |q| <= 127)."""
+    one = dev(np.array([1.0], np.float32))
+    y = host(tw.bl_bitlinear_forward_mf(dev(x), wmf_eye, one, K))
+    _, rg, _ = oracle.quant_act_int8(x)
+    scale = (rg / np.float32(127)).astype(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return y, np.rint(y.astype(np.float64) / scale[:, None])
+
+
+@pytest.mark.parametrize("M,K", [(1, 8192), (3, 2048), (8, 2048), (16, 4096)])
+def test_forward_mf_decode_quantiser_exhaustive(M, K):
+    """Every finite fp16 x against a ladder of gamma values, quantised inside the fused
+    T2-MF64 decode kernel, must give the oracle's q to the bit; then degenerate rows."""
+    wmf = tw.bl_pack_ternary_mf(dev(np.eye(K, dtype=np.int8)))
+    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite = all16[np.isfinite(all16)]
+    ladder = [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
+              np.float16(3.14), np.float16(127.0)]
+    if M > 2:
+        ladder = ladder[:3]
+    for gamma in ladder:
+        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
+        per = K - 1
+        rows = [xs[i:i + per] for i in range(0, xs.size, per)]
+        say("mf decode quant exhaustive", M, K, gamma, xs.size, len(rows))
+        for r0 in range(0, len(rows), M):
+            x = np.zeros((M, K), np.float16)
+            x[:, K - 1] = gamma
+            for m, chunk in enumerate(rows[r0:r0 + M]):
+                x[m, :chunk.size] = chunk
+            rq, _, _ = oracle.quant_act_int8(x)
+            _, q = _mf_q(x, wmf, K)
+            assert np.array_equal(q, rq.astype(np.float64)), (gamma, r0)
+    # degenerate rows: all zero, one NaN, one inf
+    x = synth.normal_fp16((M, K), 0, 95, 1)
+    x[0] = 0
+    if M > 1:
+        x[M - 1, 17] = np.float16(np.nan)
+    if M > 2:
+        x[1, 5] = np.float16(-np.inf)
+    y, q = _mf_q(x, wmf, K)
+    rq, rg, _ = oracle.quant_act_int8(x)
+    assert np.array_equal(y[0], np.zeros(K, np.float32))
+    for m in range(1, M):
+        if np.isnan(rg[m]):
+            assert np.all(np.isnan(y[m]))
+        else:
+            assert np.array_equal(q[m], rq[m].astype(np.float64))
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 512, 512), (32, 320, 1024), (64, 1024, 8192),
