@@ -333,8 +333,11 @@ int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void*
     return BL_ERR_ALIAS;
   char* w = static_cast<char*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  // decode: one launch quantises and multiplies (the weights are read once for M <= 16)
-  if (mf_decode_fits(M, N, K))
+  // decode: one launch quantises and multiplies. Each workgroup quantises its K range of
+  // every row itself, so beyond two rows that pays only where few workgroups share a range
+  // (measured on MI355X, 70B-shaped linears at M = 8: 10 % faster than quantiser + product
+  // launches for q|k|v and o, 20-35 % slower for gate|up and down)
+  if (mf_decode_fits(M, N, K) && (M <= 2 || (K <= 8192 && N / 64 < 512)))
     return check_launch(launch_mf_decode(x, static_cast<int>(M), K, wmf, beta, beta_len, N, y,
                                          reinterpret_cast<uint64_t*>(w + L.acc_off), s),
                         "bl_bitlinear_forward_mf");

@@ -155,6 +155,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// Sum over each group of eight lanes 8k .. 8k + 7, returned to every lane of the group
+// (DPP: pairs, quads, then the mirrored half row).
+__device__ __forceinline__ int group8_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false);
+  return v;
+}
+
 // popcount(x) + acc in one v_bcnt_u32_b32 (its second operand accumulates). Written out:
 // the compiler sums pairs of popcounts with a three-input add instead, one more VALU op
 // per pair in the add-only loops.

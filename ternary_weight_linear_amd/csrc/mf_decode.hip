@@ -49,7 +49,14 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit elements
 // q of a workgroup's whole K range sits in LDS: at most kMaxTiles(MR) tiles (48 KiB).
 template <int MR>
 constexpr int mfd_max_tiles() { return 48 * 1024 / (MR * 64); }
-constexpr int kXR = 4;   // quantisation steps whose x is loaded before the weights
+#ifndef BL_MFD_XR
+#define BL_MFD_XR 2
+#endif
+#ifndef BL_MFD_PRE
+#define BL_MFD_PRE 1
+#endif
+constexpr int kXR = BL_MFD_XR;     // quantisation steps whose x is loaded before the weights
+constexpr int kPre = BL_MFD_PRE;   // weight batches issued before gamma is folded
 
 template <int MR, int GL>
 __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
@@ -136,16 +143,22 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
         if (lane == 0) red_max[wave][m0 + mm] = v;
       }
     };
+    // kPre weight batches are issued behind the x loads (vector loads complete in issue
+    // order, so the folds wait only for x); the rest of the ring goes out between the
+    // quantisation steps: the texture path takes ~16 cycles per KiB per CU, and a longer
+    // queue in front would hold the gamma loads of the other waves back
     if constexpr (MR == RG) {   // every row in one go, issued before the weights
       issue_rows(0);
 #pragma unroll
       for (int r = 0; r < kXR; ++r) xv[r] = load_unit(r);
-      load_batch(w[0], 0);
+#pragma unroll
+      for (int r = 0; r < kPre; ++r) load_batch(w[r], r * kMBatch);
       fold_rows(0);
     } else {
 #pragma unroll
       for (int r = 0; r < kXR; ++r) xv[r] = load_unit(r);
-      load_batch(w[0], 0);
+#pragma unroll
+      for (int r = 0; r < kPre; ++r) load_batch(w[r], r * kMBatch);
 #pragma unroll 1
       for (int m0 = 0; m0 < MR; m0 += RG) {
         issue_rows(m0);
@@ -198,25 +211,39 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
           make_uint2(d0, d1);
     }
   };
-  // the first kXR steps from registers, the rest of the ring's batches issued between
-  // them; further steps (long ranges, many rows) load as they go
+  // the first kXR steps from registers; further steps (long ranges, many rows) load as
+  // they go
   static_assert(kXR % kQR == 0, "steps keep their row parity");
 #pragma unroll
   for (int r = 0; r < kXR; ++r) {
-    if (r + 1 < kMRing) load_batch(w[r + 1], (r + 1) * kMBatch);
+    if (kPre + r < kMRing) load_batch(w[kPre + r], (kPre + r) * kMBatch);
     if (r < nsteps) quantise(xv[r], r, r % kQR);
   }
 #pragma unroll
-  for (int r = kXR + 1; r < kMRing; ++r) load_batch(w[r], r * kMBatch);
+  for (int r = kPre + kXR; r < kMRing; ++r) load_batch(w[r], r * kMBatch);
   for (int r = kXR; r < nsteps; r += kQR) {
 #pragma unroll
     for (int p = 0; p < kQR; ++p)
       if (r + p < nsteps) quantise(load_unit(r + p), r + p, p);
   }
+  // the rows' sums: lanes 8k .. 8k + 7 share a unit row, (8p + k) % MR for parity p; sum
+  // each group of eight with DPP, gather the groups in scalars, one LDS add per row
+  // (a same-address LDS atomic from every lane is compiled into a 64-step scalar loop)
+  {
+    int rs[MR];
 #pragma unroll
-  for (int p = 0; p < kQR; ++p) {
-    if (unit_row(p) < M)
-      __hip_atomic_fetch_add(&rsum[unit_row(p)], qs[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int m = 0; m < MR; ++m) rs[m] = 0;
+#pragma unroll
+    for (int p = 0; p < kQR; ++p) {
+      const int v = group8_sum_i32(qs[p]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rs[(8 * p + k) % MR] += __builtin_amdgcn_readlane(v, 8 * k);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (m < M) __hip_atomic_fetch_add(&rsum[m], rs[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
   }
   __syncthreads();
 
@@ -250,27 +277,24 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
       }
     }
   }
-  __syncthreads();   // every wave is done with q
-
-  // The sums leave through LDS (q is no longer needed), lane = column: each lane then
-  // hands over at most MR outputs, all of them live for rows < M. From the MFMA layout
-  // directly a lane would hold 16 outputs, most of them for rows past M.
-  int* st = reinterpret_cast<int*>(qb) + wave * MR * 64;
-  static_assert(kMW * MR * 64 * 4 <= kMaxTiles * MR * 64, "staging fits the q buffer");
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {   // output k = 4 f + i: row 4g + i, column 16 f + u
-    const int f = k / 4, i = k % 4;
-    const int row = 4 * g + i;
-    if (row < M) st[row * 64 + 16 * f + u] = (acc[f][i] >> (2 * f)) - (f < 3 ? rsum[row] : 0);
-  }
-  __syncthreads();
   if (!active) return;
+  // Outputs to lane = column within the wave (ds_bpermute, no LDS traffic between waves):
+  // row m, column 16f + u sits in lane 16 (m / 4) + u, element m % 4 of fragment f. Each
+  // lane then hands over at most MR outputs, all of them live for rows < M (from the MFMA
+  // layout directly a lane would hold 16 outputs, most of them for rows past M).
   const int64_t col = band * 64 + lane;
   int32_t v[MR];
   uint32_t live = 0;
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    v[m] = m < M ? st[m * 64 + lane] : 0;
+    const int src = (16 * (m >> 2) + (lane & 15)) * 4;
+    int got = 0;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int t = __builtin_amdgcn_ds_bpermute(src, (acc[f][m & 3] >> (2 * f)) - (f < 3 ? rsum[min(m, MR - 1)] : 0));
+      got = (lane >> 4) == f ? t : got;
+    }
+    v[m] = got;
     if (m < M) live |= 1u << m;
   }
   auto word = [&](int m) __attribute__((always_inline)) {
