@@ -428,7 +428,8 @@ def bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, beta, N: int, want_y: bool = Tru
 
 
 def bl_bitlinear_forward_mf(x, wmf, beta, N: int, out=None):
-    """fp16 x [M, K] -> y fp32 [M, N] from T2-MF64 weights: quantise + matrix-core product."""
+    """fp16 x [M, K] -> y fp32 [M, N] from T2-MF64 weights: one fused quantise + matrix-core
+    launch at decode sizes (see the header), else quantiser + matrix-core product."""
     _half_bits(x, "x")
     _need(wmf, torch.uint8, "wmf")
     d = _dev(x, wmf, beta)

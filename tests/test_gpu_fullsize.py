@@ -1,10 +1,11 @@
 """Full-size parity in the launch configuration the benchmark times.
 
 One layer of the 70B-shaped stack is built exactly as bench.py builds it (GPU counter-based
-codes, packed into stacked q|k|v and gate|up buffers) and run through the same entry points
-(fused quantise + GEMV at M = 1, quantiser + int8-MFMA GEMM at M = 8 and 64). Sampled output
-rows are recomputed by the oracle from codes regenerated on the host. The graph-replayed
-pass is checked bit-for-bit against eager launches over several replays."""
+codes, packed into stacked q|k|v and gate|up buffers, repacked into T2-MF64) and run through
+the same entry points (the fused T2-MF64 decode kernel at M = 1, the benchmark's default
+pass; the add-only GEMV; quantiser + int8-MFMA products at M = 8 and 64). Sampled output
+rows are recomputed by the oracle from codes regenerated on the host. Graph-replayed passes
+are checked bit-for-bit against eager launches over several replays."""
 import numpy as np
 import pytest
 import torch
@@ -135,16 +136,55 @@ def test_stack_kernel_full_size(layer0, M):
             assert_rel(host(y)[:, ids], yref)
 
 
-@pytest.mark.parametrize("M", [8, 64])
+@pytest.mark.parametrize("M", [1, 2, 8, 64])
 def test_mf_layer_sampled_rows(layer0, M):
-    """The 70B layer repacked into T2-MF64 (the benchmark's batched-decode configuration):
-    quantiser + matrix-core product, sampled rows against the oracle."""
+    """The 70B layer repacked into T2-MF64 (the benchmark's default pass at M = 1, its
+    batched decode at M = 8, 64): sampled rows against the oracle; at M <= 2 every output
+    bitwise equal to the add-only GEMV from T2-PN-64 (same integers, same epilogue)."""
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
     for gi, (gname, buf, N, K, parts) in enumerate(layer0):
         say("fullsize mf", gname, "M", M)
         wmf = tw.bl_repack_ternary_mf(buf, N, K)
         x16 = synth.normal_fp16((M, K), 0, 5, 4000, gi)
-        y = tw.bl_bitlinear_forward_mf(torch.from_numpy(x16).to(DEV), wmf, beta, N)
+        x = torch.from_numpy(x16).to(DEV)
+        y = tw.bl_bitlinear_forward_mf(x, wmf, beta, N)
         ids, yref = _sampled_reference(x16, parts, K, 32, seed=200 + gi + 10 * M)
         assert_rel(host(y)[:, ids], yref)
+        if M <= 2:
+            ref = tw.bl_bitlinear_forward(x, buf, beta, N, path=tw.BL_PATH_GEMV)
+            assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), gname
         del wmf
+
+
+def test_mf_layer_graph_replays_match_eager(layer0):
+    """The benchmark's default pass for one layer: four fused T2-MF64 decode launches
+    captured in a HIP graph; every replay, with eager work and synchronisations between
+    replays, must reproduce the eager outputs bitwise."""
+    say("fullsize: mf graph replay")
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
+    wmfs = [tw.bl_repack_ternary_mf(buf, N, K) for (_, buf, N, K, _) in layer0]
+    xs = [torch.from_numpy(synth.normal_fp16((1, K), 0, 5, 5000, gi)).to(DEV)
+          for gi, (_, _, _, K, _) in enumerate(layer0)]
+    ys = [torch.empty((1, N), dtype=torch.float32, device=DEV) for (_, _, N, _, _) in layer0]
+
+    def run():
+        for (gname, buf, N, K, parts), w, x, y in zip(layer0, wmfs, xs, ys):
+            tw.bl_bitlinear_forward_mf(x, w, beta, N, out=y)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.int32), e.view(torch.int32)), f"replay {rep} differs"
+        tmp = torch.randn(1 << 20, device=DEV).sum()       # eager work between replays
+        torch.cuda.synchronize()
+        del tmp
+    del wmfs
