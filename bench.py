@@ -309,12 +309,19 @@ def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
 
 def bench_decode7b_stack(torch, tw, sgpu, synth, dev, steps, warmup):
     """The LLaMA-7B-shaped model decoded at M = 1: 32 layers (1.62 GB packed, > the 256 MB
-    MALL) in model order, q|k|v and gate|up stacked, one fused quantise + GEMV launch per
-    group, replayed from a HIP graph (the same pass as the 70B line)."""
+    MALL) in model order, q|k|v and gate|up stacked, one fused launch per group replayed
+    from a HIP graph: the T2-MF64 decode kernel (the same pass as the 70B line) and, for
+    comparison, the add-only GEMV from T2-PN-64."""
     layers = build_stack(torch, tw, sgpu, synth, dev, synth.LLAMA7B_LINEARS, 32, 3)
+    layers_mf = repack_stack_mf(torch, tw, dev, layers)
+    r = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, 1, steps, warmup)
+    del layers_mf
+    out = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs", "launches_per_pass", "weight_bytes")}
+    out["weights"] = "T2-MF64"
     r = bench_decode70b(torch, tw, synth, dev, layers, 1, steps, warmup)
+    out["t2pn_gemv"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs")}
     del layers
-    return {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs", "launches_per_pass", "weight_bytes")}
+    return out
 
 
 def bench_decode7b(torch, tw, sgpu, synth, dev, steps, warmup, pool=32):
@@ -593,7 +600,7 @@ def main():
         extra["prefill3b_m512"] = bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup)
         log("prefill3b:", json.dumps(extra["prefill3b_m512"]))
         extra["decode7b_m1"] = bench_decode7b_stack(torch, tw, sgpu, synth, dev, args.steps, args.warmup)
-        log("decode7b (32 layers, stacked, fused):", json.dumps(extra["decode7b_m1"]))
+        log("decode7b (32 layers, stacked, fused launches):", json.dumps(extra["decode7b_m1"]))
         extra["decode7b_m1_pool32"] = bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup)
         log("decode7b (7 GEMV launches per layer):", json.dumps(extra["decode7b_m1_pool32"]))
         extra["onebit4096_pool256"] = bench_onebit(torch, tw, synth, dev, args.steps, args.warmup)
