@@ -164,6 +164,17 @@ __device__ __forceinline__ int group8_sum_i32(int v) {
   return v;
 }
 
+// Sum over the 64 lanes of a wave, returned to every lane: the eight-lane sums, then the
+// mirrored row, then the row broadcasts into lanes of rows 1, 3 and 2, 3 (lanes a broadcast
+// does not write add 0), leaving the total in lane 63.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v = group8_sum_i32(v);
+  v += __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // popcount(x) + acc in one v_bcnt_u32_b32 (its second operand accumulates). Written out:
 // the compiler sums pairs of popcounts with a three-input add instead, one more VALU op
 // per pair in the add-only loops.

@@ -128,8 +128,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < 4; ++j) mb = max(mb, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, off)));
+  mb = wave_max_u32(mb);
   if (lane == 0) red_max[wave] = mb;
   __syncthreads();
   mb = red_max[0];
@@ -158,8 +157,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
     if (q) *reinterpret_cast<uint2*>(q + m * K + 8 * i) = make_uint2(packed[0], packed[1]);
   }
   if (rowsum) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    sum = wave_sum_i32(sum);
     if (lane == 0) red_sum[wave] = sum;
     __syncthreads();
     if (threadIdx.x == 0) {
