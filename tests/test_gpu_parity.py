@@ -694,14 +694,18 @@ def test_gemm_mf_acc_and_output(M, N, K):
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
 
 
-# Decode through T2-MF64 (M <= 16: one fused launch). Shapes: one tile; ragged band groups
-# (inactive waves) with long rows (row loads past 8192 inputs); the largest K; several
-# chunks per workgroup (K split in two over wide outputs); no K split at all (>= 512 band
-# groups); every row-tile width 1, 2, 4, 8, 16 with unused rows.
+# Decode through T2-MF64. The fused kernel takes M <= 2, and M <= 16 where K <= 8192 and
+# the output has < 512 bands; the other shapes go through quantiser + product. Fused
+# shapes: one tile; ragged band groups (inactive waves) with long rows (row loads past 8192
+# inputs); the largest K; long K ranges per workgroup (K split in two over wide outputs);
+# no K split (>= 512 band groups at M = 1; a 4-tile K at M = 16); ranges past the LDS
+# capacity of 16 rows (more splits); every row-tile width 1, 2, 4, 8, 16 with unused rows.
+# Routed elsewhere: long or wide shapes at M > 2, and M x N past the split words' capacity.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 320, 8256), (2, 128, 28672),
-                                   (1, 65536, 16384), (3, 65536, 16384), (8, 65536, 8192),
-                                   (16, 65536, 8192), (1, 131072, 256), (5, 448, 4160),
-                                   (13, 192, 2048), (4, 10240, 8192)])
+                                   (1, 65536, 16384), (1, 131072, 256), (16, 2048, 256),
+                                   (16, 32704, 8192), (8, 32704, 8192), (5, 448, 4160),
+                                   (13, 192, 2048), (4, 10240, 8192), (3, 65536, 16384),
+                                   (8, 65536, 8192), (16, 262208, 4096)])
 def test_forward_mf_decode_equals_forward(M, N, K):
     """The fused decode kernel gives the outputs of the unfused T2-PN-64 path to the bit and
     matches the oracle on sampled rows."""
