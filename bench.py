@@ -2,18 +2,18 @@
 """Benchmark of the BitLinear hot path on one MI355X.
 
 Default workload: the 70B-shaped ternary stack (80 layers x q 8192x8192, k/v 1024x8192,
-o 8192x8192, gate/up 28672x8192, down 8192x28672, 2-bit packed T2-MF64, 17,112,760,320
+o 8192x8192, gate/up 28672x8192, down 8192x28672, 2-bit packed T2-PN-64, 17,112,760,320
 bytes) decoded at M=1 token. One step = one pass over all 80 layers; each layer runs four
 dependent linear groups in model order (stacked q|k|v, o, stacked gate|up, down), each one
-launch of the fused quantise + int8 matrix-core decode kernel (bl_bitlinear_forward_mf);
-the pass is replayed from a HIP graph. The metric is effective HBM GB/s = algorithmic
-bytes of the pass / pass time.
+launch of the fused quantise + add-only GEMV (int32 accumulation by select + popcount, no
+multiplies); the pass is replayed from a HIP graph. The metric is effective HBM GB/s =
+algorithmic bytes of the pass / pass time.
 
-The same JSON line carries the other measured workloads under "extra": the same pass
-through the add-only GEMV from T2-PN-64 weights and as one persistent launch; the stack at
-M = 8, 32, 64 (tokens/s); the 3B-shaped prefill at M = 512 (int8 TOPS); the 7B-shaped
-decode set, the OneBit and residual 4096x4096 layers and SVID; a "roofline" object for the
-dominant kernel and a "cpu_baseline" object for the CPU oracle.
+The same JSON line carries the other measured workloads under "extra": the same pass on the
+int8 matrix cores from T2-MF64 weights (bl_bitlinear_forward_mf) and as one persistent
+launch; the stack at M = 8, 32, 64 (tokens/s); the 3B-shaped prefill at M = 512 (int8
+TOPS); the 7B-shaped decode set, the OneBit and residual 4096x4096 layers and SVID; a
+"roofline" object for the dominant kernel and a "cpu_baseline" object for the CPU oracle.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-extra] [--only NAME]
 """
@@ -34,8 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "BitLinear GEMV effective HBM GB/s (% peak); int8 TOPS at M=512 (% peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mf_decode_decode70b_m1_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", "mf_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode70b_m1_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", "gemv.hip")
 
 
 def log(*a):
@@ -570,15 +570,15 @@ def main():
         print(json.dumps({args.only: res}))
         return
 
-    layers_mf = repack_stack_mf(torch, tw, dev, layers)
-    log("repacked into T2-MF64")
-    main_res = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, 1, args.steps, args.warmup,
-                                  use_graph=not args.no_graph)
+    main_res = bench_decode70b(torch, tw, synth, dev, layers, 1, args.steps, args.warmup,
+                               use_graph=not args.no_graph)
     log("decode70b M=1:", json.dumps(main_res))
     if not args.skip_extra:
-        r = bench_decode70b(torch, tw, synth, dev, layers, 1, args.steps, args.warmup)
-        extra["decode70b_m1_t2pn_gemv"] = {k: r[k] for k in ("ms_per_pass", "ms_per_pass_eager", "tokens_per_s", "gbs")}
-        log("decode70b M=1, add-only GEMV (T2-PN-64 weights):", json.dumps(extra["decode70b_m1_t2pn_gemv"]))
+        layers_mf = repack_stack_mf(torch, tw, dev, layers)
+        r = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, 1, args.steps, args.warmup)
+        extra["decode70b_m1_mfma"] = {k: r[k] for k in ("ms_per_pass", "ms_per_pass_eager", "tokens_per_s", "gbs")}
+        extra["decode70b_m1_mfma"]["weights"] = "T2-MF64"
+        log("decode70b M=1, int8 matrix cores (T2-MF64 weights):", json.dumps(extra["decode70b_m1_mfma"]))
         r = bench_decode70b_stack(torch, tw, synth, dev, layers, 1, args.steps, args.warmup)
         extra["decode70b_m1_stack"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs", "launches_per_pass")}
         del r
@@ -593,7 +593,7 @@ def main():
             extra[f"decode70b_m{M}"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs")}
             extra[f"decode70b_m{M}"]["weights"] = "T2-MF64"
             log(f"decode70b M={M} (T2-MF64 weights):", json.dumps(extra[f'decode70b_m{M}']))
-    del layers_mf
+        del layers_mf
     del layers
     torch.cuda.empty_cache()
     if not args.skip_extra:
@@ -630,14 +630,14 @@ def main():
         "data": "synthetic: seeded counter-based ternary codes (P(0)=P(+-1)=1/3), fp16 N(0,1) activations",
         "config": {"workload": "b1.58 70B-shaped full stack decode, M=1 token, 80 layers x "
                                "(qkv 10240x8192, o 8192x8192, gate|up 57344x8192, down 8192x28672)",
-                   "weights": "T2-MF64 (2 bits per weight)",
+                   "weights": "T2-PN-64 (2 bits per weight)",
                    "weight_bytes_per_pass": main_res["weight_bytes"],
                    "algorithmic_bytes_per_pass": main_res["algo_bytes"],
                    "launches_per_pass": main_res["launches_per_pass"],
                    "tokens_per_s": round(main_res["tokens_per_s"], 2),
                    "frac_hbm_peak": round(main_res["gbs"] / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm",
-                     "kernel": "mf_decode_kernel<1, GL> (quantise + int8 matrix-core product, T2-MF64)",
+                     "kernel": "gemv_fused_kernel<1, GL> (quantise + add-only GEMV, T2-PN-64)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
