@@ -2,10 +2,11 @@
 
 One layer of the 70B-shaped stack is built exactly as bench.py builds it (GPU counter-based
 codes, packed into stacked q|k|v and gate|up buffers, repacked into T2-MF64) and run through
-the same entry points (the fused T2-MF64 decode kernel at M = 1, the benchmark's default
-pass; the add-only GEMV; quantiser + int8-MFMA products at M = 8 and 64). Sampled output
-rows are recomputed by the oracle from codes regenerated on the host. Graph-replayed passes
-are checked bit-for-bit against eager launches over several replays."""
+the same entry points (the fused quantise + add-only GEMV at M = 1, the benchmark's default
+pass; the fused T2-MF64 matrix-core decode at M = 1, 2, its comparison line; quantiser +
+int8-MFMA products at M = 8 and 64). Sampled output rows are recomputed by the oracle from
+codes regenerated on the host. Graph-replayed passes are checked bit-for-bit against eager
+launches over several replays."""
 import numpy as np
 import pytest
 import torch
@@ -138,8 +139,8 @@ def test_stack_kernel_full_size(layer0, M):
 
 @pytest.mark.parametrize("M", [1, 2, 8, 64])
 def test_mf_layer_sampled_rows(layer0, M):
-    """The 70B layer repacked into T2-MF64 (the benchmark's default pass at M = 1, its
-    batched decode at M = 8, 64): sampled rows against the oracle; at M <= 2 every output
+    """The 70B layer repacked into T2-MF64 (the benchmark's matrix-core decode line at M = 1,
+    its batched decode at M = 8, 64): sampled rows against the oracle; at M <= 2 every output
     bitwise equal to the add-only GEMV from T2-PN-64 (same integers, same epilogue)."""
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
     for gi, (gname, buf, N, K, parts) in enumerate(layer0):
@@ -157,9 +158,9 @@ def test_mf_layer_sampled_rows(layer0, M):
 
 
 def test_mf_layer_graph_replays_match_eager(layer0):
-    """The benchmark's default pass for one layer: four fused T2-MF64 decode launches
-    captured in a HIP graph; every replay, with eager work and synchronisations between
-    replays, must reproduce the eager outputs bitwise."""
+    """The benchmark's matrix-core decode line for one layer: four fused T2-MF64 decode
+    launches captured in a HIP graph; every replay, with eager work and synchronisations
+    between replays, must reproduce the eager outputs bitwise."""
     say("fullsize: mf graph replay")
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
     wmfs = [tw.bl_repack_ternary_mf(buf, N, K) for (_, buf, N, K, _) in layer0]
