@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
 
 // ---- T2-MF64 with q staged in LDS (batched decode, prefill) -----------------------------
 // A workgroup of four waves owns four consecutive bands (one per wave), 16 FM rows of q
-// (FM = 1 or 2; more rows take more workgroups) and a K range. For each chunk of kQC tiles the
+// (FM = 1, 2 or 3; more rows take more workgroups) and a K range. For each chunk of kQC tiles the
 // workgroup copies q[rows, chunk] into LDS once; each wave decodes its own weight tile once
 // (16 ALU ops) and runs FM x 4 MFMAs with A fragments read from LDS, so neither the q bytes
 // nor the decoding are repeated per 16 rows. Weights come through a buffer resource over
@@ -612,7 +612,11 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
 // still gives >= 192 workgroups (the decoded weights serve more rows), else 16 (row groups
 // of a band group share its weights through one XCD's L2, and more workgroups win).
 int mfq_fm(int64_t M, int64_t groups) {
-  if (g_mf_fm > 0) return g_mf_fm > 1 ? 2 : 1;
+  if (g_mf_fm > 0) return g_mf_fm > 2 ? 3 : g_mf_fm;
+  // measured on MI355X: 48-row tiles for prefill-sized M over wide outputs (3B gate|up at
+  // M = 512: 43.4 vs 46.3 us; narrower outputs and 64-row tiles were slower), 32-row tiles
+  // for 17-64 rows where they still give enough work items, else 16
+  if (M >= 256 && groups >= 64) return 3;
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 
@@ -640,8 +644,10 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
   if (fm == 1)
     hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum);
-  else
+  else if (fm == 2)
     hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum);
+  else
+    hipLaunchKernelGGL((tern_mfq_kernel<3>), grid, dim3(256), 0, s, a, rowsum);
   return hipGetLastError();
 }
 

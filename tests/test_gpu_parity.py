@@ -710,6 +710,20 @@ def test_forward_mf_decode_equals_forward(M, N, K):
     """The fused decode kernel gives the outputs of the unfused T2-PN-64 path to the bit and
     matches the oracle on sampled rows."""
     say("forward mf decode", M, N, K)
+    _mf_vs_pn_sampled(M, N, K)
+
+
+# Prefill-sized M through T2-MF64: 48-row tiles of the staged-q kernel over wide outputs
+# (ragged: 300 = 6 x 48 + 12), the 3B gate|up shape at M = 512.
+@pytest.mark.parametrize("M,N,K", [(300, 16384, 320), (512, 17280, 3200)])
+def test_forward_mf_prefill_equals_forward(M, N, K):
+    say("forward mf prefill", M, N, K)
+    _mf_vs_pn_sampled(M, N, K)
+
+
+def _mf_vs_pn_sampled(M, N, K):
+    """T2-MF64 forward bitwise equal to the T2-PN-64 forward on the same GPU-drawn codes, and
+    97 sampled output columns against the oracle from codes regenerated on the host."""
     x = synth.normal_fp16((M, K), 0, 135, M, K)
     key = synth.matrix_key(0, 136, N, K)
     codes_d = sgpu.ternary_codes(key, N, K, DEV)     # the GPU twin of synth.ternary_codes
