@@ -352,14 +352,17 @@ __global__ __launch_bounds__(256) void tern_mf_kernel(const TernArgs a,
 constexpr int kQC = 4;                     // tiles per q chunk and per weight batch
 constexpr int kQPitch = kQC * 64 + 16;     // bytes per staged row of q
 constexpr int kStRow = 68;                 // ints per staged result row (64 + 4)
-constexpr int kQRing = 4;                  // chunks in flight per wave
+constexpr int kQRing = 4;                  // chunks in flight per wave (16- and 32-row tiles)
+constexpr int kQRing3 = 2;                 // 48-row tiles: two, so that three waves fit per SIMD
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elements
 
+// 48-row tiles are held to 168 VGPRs (three workgroups per CU instead of two): a 3B-shaped
+// prefill then runs its work items in one round instead of one and a half.
 template <int FM>
-__global__ __launch_bounds__(256) void tern_mfq_kernel(const TernArgs a,
-                                                       const int32_t* __restrict__ rowsum) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 3 ? 3 : 1)))
+void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   constexpr int kRows = 16 * FM;
-  constexpr int R = kQRing;
+  constexpr int R = FM == 3 ? kQRing3 : kQRing;
   constexpr int kSegs = kRows * kQC * 4 / 256;   // 16-byte pieces of q per thread per chunk
   static_assert(kSegs >= 1 && (kRows * kQC * 4) % 256 == 0, "q chunk copy");
   constexpr int kQBuf = kRows * kQPitch;           // one staged chunk of q
@@ -613,10 +616,11 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
 // of a band group share its weights through one XCD's L2, and more workgroups win).
 int mfq_fm(int64_t M, int64_t groups) {
   if (g_mf_fm > 0) return g_mf_fm > 2 ? 3 : g_mf_fm;
-  // measured on MI355X: 48-row tiles for prefill-sized M over wide outputs (3B gate|up at
-  // M = 512: 43.4 vs 46.3 us; narrower outputs and 64-row tiles were slower), 32-row tiles
-  // for 17-64 rows where they still give enough work items, else 16
-  if (M >= 256 && groups >= 64) return 3;
+  // measured on MI355X: 48-row tiles for prefill-sized M over >= 32 band groups (3B at
+  // M = 512: gate|up 34.2 vs 46.3 us with 16-row tiles, q|k|v 26.8 vs 28.0 us; o and down,
+  // 13 groups, too few work items, were slower; 64-row tiles were slower everywhere),
+  // 32-row tiles for 17-64 rows where they still give enough work items, else 16
+  if (M >= 256 && groups >= 32) return 3;
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 

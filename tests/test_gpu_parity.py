@@ -713,9 +713,11 @@ def test_forward_mf_decode_equals_forward(M, N, K):
     _mf_vs_pn_sampled(M, N, K)
 
 
-# Prefill-sized M through T2-MF64: 48-row tiles of the staged-q kernel over wide outputs
-# (ragged: 300 = 6 x 48 + 12), the 3B gate|up shape at M = 512.
-@pytest.mark.parametrize("M,N,K", [(300, 16384, 320), (512, 17280, 3200)])
+# Prefill-sized M through T2-MF64: 48-row tiles of the staged-q kernel over >= 32 band
+# groups (ragged: 300 = 6 x 48 + 12; exactly 32 groups with a 17-tile K, an odd number of
+# two-chunk ring turns), the 3B q|k|v and gate|up shapes at M = 512.
+@pytest.mark.parametrize("M,N,K", [(300, 16384, 320), (300, 8192, 1088), (512, 9600, 3200),
+                                   (512, 17280, 3200)])
 def test_forward_mf_prefill_equals_forward(M, N, K):
     say("forward mf prefill", M, N, K)
     _mf_vs_pn_sampled(M, N, K)
