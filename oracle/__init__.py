@@ -29,7 +29,8 @@ from .b158 import (QB, exact_abs_sum, f32_nearest, absmean_beta, ternarize_absme
 from .onebit import (onebit_forward, onebit_error_scale, onebit_storage_bits,
                      onebit_param_count, svid_rank1)
 from .billm import (residual_binarize, residual_forward, residual_error_scale,
-                    pairwise_sum_f32, billm_storage_bits_per_param)
+                    group_abs_mean_f32, exact_group_abs_sums, f32_nearest_dyadic,
+                    billm_storage_bits_per_param)
 
 __all__ = [
     "pack_ternary", "unpack_ternary", "pack_sign", "unpack_sign", "act_planes",
@@ -38,5 +39,6 @@ __all__ = [
     "quant_act_int8", "acc_exact", "bitlinear_output", "bitlinear_forward",
     "onebit_forward", "onebit_error_scale", "onebit_storage_bits", "onebit_param_count",
     "svid_rank1", "residual_binarize", "residual_forward", "residual_error_scale",
-    "pairwise_sum_f32", "billm_storage_bits_per_param",
+    "group_abs_mean_f32", "exact_group_abs_sums", "f32_nearest_dyadic",
+    "billm_storage_bits_per_param",
 ]

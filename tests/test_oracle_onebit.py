@@ -4,6 +4,8 @@ import json
 import math
 import os
 
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -120,19 +122,120 @@ def test_billm_storage_golden():
     assert round(n_store, g["printed_decimals"]) == g["n_storing_printed"]
 
 
-def test_pairwise_sum_within_its_error_bound():
-    """The fp32 pairwise tree is within log2(n) * 2^-24 * sum|a| of the exact sum, and
-    equals it when every partial sum is exact (small integers)."""
-    from fractions import Fraction
+def _fraction_mean_f32(row):
+    """Independent route to the group mean: a Fraction sum of every element, one division,
+    then the general rational-to-fp32 rounding."""
+    total = sum((Fraction(float(abs(v))) for v in row), Fraction(0))
+    return oracle.f32_nearest(total / len(row))
+
+
+def test_group_sums_match_per_exponent_sums():
+    """The limb sums equal the per-exponent exact sum (and a Fraction sum) on groups that
+    span the whole fp32 range: subnormals, the largest finite value, zeros of both signs."""
     rg = synth.rng(6, 3)
-    a = (rg.standard_normal((40, 128)) * np.exp2(rg.integers(-20, 20, (40, 128)))).astype(np.float32)
-    got = oracle.pairwise_sum_f32(a)
-    for row, s in zip(a, got):
-        exact = sum((Fraction(float(v)) for v in row), Fraction(0))
-        bound = 7 * 2.0 ** -24 * float(sum(abs(float(v)) for v in row))
-        assert abs(float(Fraction(float(s)) - exact)) <= bound
-    ints = rg.integers(-1000, 1000, (5, 128)).astype(np.float32)
-    assert np.array_equal(oracle.pairwise_sum_f32(ints), ints.astype(np.int64).sum(1).astype(np.float32))
+    a = (rg.standard_normal((24, 128)) * np.exp2(rg.integers(-149, 127, (24, 128)))).astype(np.float32)
+    a[0] = np.float32(3.4028235e38)                        # 128 x FLT_MAX: the largest sum
+    a[1, :64] = np.float32(1e-45)                          # smallest subnormal
+    a[2, ::2] = -0.0
+    sums = oracle.exact_group_abs_sums(a)
+    for row, S in zip(a, sums):
+        assert Fraction(S, 1 << 149) == oracle.exact_abs_sum(row)
+        assert Fraction(S, 1 << 149) == sum((Fraction(float(abs(v))) for v in row), Fraction(0))
+
+
+def test_f32_nearest_dyadic_matches_rational_rounding():
+    rg = synth.rng(6, 4)
+    cases = [(int(s), int(k)) for s, k in zip(rg.integers(1, 1 << 62, 300), rg.integers(0, 300, 300))]
+    cases += [((1 << 24) + 1, 1), ((1 << 24) + 3, 1), ((1 << 25) - 1, 2),   # ties; carry to 2^24
+              (1, 149), (1, 150), (3, 150), (1, 151), ((1 << 23) - 1, 149),  # subnormal grid
+              ((1 << 24) - 1, 150), ((1 << 24) - 1, 149 + 7), (0xFFFFFF << 104, 0),  # FLT_MAX
+              (0xFFFFFF8 << 100, 0)]                                         # rounds to inf
+    for S, k in cases:
+        got = oracle.f32_nearest_dyadic(S, k)
+        want = oracle.f32_nearest(Fraction(S, 1 << k))
+        assert got.view(np.uint32) == want.view(np.uint32), (S, k)
+
+
+def test_group_mean_is_exact_rational_mean():
+    """alpha = the fp32 value nearest the exact group mean. The constructed groups separate
+    it from any fp32 summation order: tiny terms that an fp32 running sum (sequential or
+    pairwise) absorbs, and exact ties broken to even."""
+    rg = synth.rng(6, 5)
+    groups = [(rg.standard_normal(128) * np.exp2(rg.integers(-140, 100, 128))).astype(np.float32)
+              for _ in range(20)]
+    g = np.full(128, np.float32(2.0 ** -25)); g[0] = 1.0
+    groups.append(g)                       # mean 2^-7 + 127 * 2^-32: not 2^-7 (sequential fp32)
+    t = np.ones(128, np.float32); t[5] = np.float32(1 + 2.0 ** -17)
+    groups.append(t)                       # mean 1 + 2^-24, a tie: even -> 1.0
+    t3 = np.ones(128, np.float32); t3[9] = np.float32(1 + 3 * 2.0 ** -17)
+    groups.append(t3)                      # mean 1 + 3 * 2^-24, a tie: even -> 1 + 2^-22
+    sub = np.zeros(128, np.float32); sub[3] = np.float32(2.0 ** -149 * 192)
+    groups.append(sub)                     # mean 1.5 * 2^-149, a subnormal tie -> 2 * 2^-149
+    a = np.stack(groups)
+    got = oracle.group_abs_mean_f32(a)
+    for row, v in zip(a, got):
+        assert v.view(np.uint32) == _fraction_mean_f32(row).view(np.uint32)
+    assert got[-4] == np.float32(2.0 ** -7 + 128 * 2.0 ** -32) != np.float32(2.0 ** -7)
+    assert got[-3] == np.float32(1.0)
+    assert got[-2] == np.float32(1 + 2.0 ** -22)
+    assert got[-1] == np.float32(2 * 2.0 ** -149)
+    seq = np.float32(0)
+    for v in g:
+        seq = np.float32(seq + v)
+    assert seq / np.float32(128) == np.float32(2.0 ** -7) != got[-4]   # an fp32 sum misses it
+    c = np.float32(0.1)
+    assert oracle.group_abs_mean_f32(np.where(rg.random(128) < 0.5, -c, c).astype(np.float32)) == c
+    bad = np.ones((3, 128), np.float32)
+    bad[0, 7], bad[1, 7], bad[2, [7, 8]] = np.nan, np.inf, [np.inf, np.nan]
+    m = oracle.group_abs_mean_f32(bad)
+    assert np.isnan(m[0]) and m[1] == np.inf and np.isnan(m[2])
+
+
+def test_onebit_error_scale_closed_forms():
+    """|h_n| * sum_k |x_k g_k|: with x = +-1 alternating, g = 2 and h = -0.5 every element's
+    scale is K although the signed sum (and y for S = 1) is 0; a dropped |.| on the sum or
+    on h would give 0 or -K. The scale bounds |y| for any S."""
+    K, N = 256, 64
+    x = np.where(np.arange(K) % 2 == 0, 1.0, -1.0).astype(np.float16)[None, :]
+    g = np.full(K, 2.0, np.float16)
+    h = np.full(N, -0.5, np.float16)
+    sc = oracle.onebit_error_scale(x, g, h)
+    assert sc.shape == (1, N) and np.all(sc == K)
+    assert np.all(oracle.onebit_forward(x, g, np.ones((N, K), np.int8), h) == 0)
+    xs = synth.normal_fp16((3, K), 6, 7)
+    gs = synth.uniform_fp16((K,), 0.5, 1.5, 6, 8)
+    hs = -synth.uniform_fp16((N,), 0.5, 1.5, 6, 9)
+    S = np.where(synth.rng(6, 10).random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    sc = oracle.onebit_error_scale(xs, gs, hs)
+    want = np.abs(xs.astype(np.float64) * gs.astype(np.float64)).sum(1)[:, None] * np.abs(hs.astype(np.float64))[None, :]
+    assert np.allclose(sc, want, rtol=1e-15, atol=0)
+    assert np.all(np.abs(oracle.onebit_forward(xs, gs, S, hs)) <= sc * (1 + 1e-12))
+    assert np.all(np.abs(oracle.onebit_forward(xs, gs, np.ones((N, K), np.int8), -hs)) <= sc * (1 + 1e-12))
+
+
+def test_residual_error_scale_closed_forms():
+    """sum_b (|alpha_o| + |alpha_r|)[n, b] * sum_{k in b} |x_mk|: constant scales 1 give
+    2 * sum |x| (a signed sum would cancel for alternating x); one nonzero group gives
+    |alpha| times that group's sum |x|; negative scales count by magnitude."""
+    K, N = 512, 64
+    x = np.where(np.arange(K) % 2 == 0, 1.5, -1.5).astype(np.float16)[None, :]
+    ones = np.ones((N, K // 128), np.float32)
+    assert np.all(oracle.residual_error_scale(x, ones, ones) == 2 * 1.5 * K)
+    ao = np.zeros((N, K // 128), np.float32)
+    ar = np.zeros_like(ao)
+    ao[3, 2], ar[5, 1] = -0.25, 4.0
+    xs = synth.normal_fp16((2, K), 6, 11)
+    sc = oracle.residual_error_scale(xs, ao, ar)
+    gsum = np.abs(xs.astype(np.float64)).reshape(2, K // 128, 128).sum(2)
+    assert np.allclose(sc[:, 3], 0.25 * gsum[:, 2], rtol=1e-15, atol=0)
+    assert np.allclose(sc[:, 5], 4.0 * gsum[:, 1], rtol=1e-15, atol=0)
+    assert np.all(np.delete(sc, [3, 5], axis=1) == 0)
+    Bo = np.where(synth.rng(6, 12).random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    Br = np.where(synth.rng(6, 13).random((N, K)) < 0.5, -1, 1).astype(np.int8)
+    a1 = synth.uniform_fp16((N, K // 128), 0.5, 1.5, 6, 14).astype(np.float32)
+    a2 = synth.uniform_fp16((N, K // 128), 0.0, 0.5, 6, 15).astype(np.float32)
+    assert np.all(np.abs(oracle.residual_forward(xs, Bo, a1, Br, a2)) <=
+                  oracle.residual_error_scale(xs, a1, a2) * (1 + 1e-12))
 
 
 def test_residual_never_worse_than_direct():
