@@ -302,12 +302,13 @@ int bl_svid_rank1(const float* W, int64_t N, int64_t K, int iters, void* spacked
 /* Residual binarisation of a float weight ([billm] "方法细节", step 2, binary residual
  * approximation): W ~ alpha_o ⊙ B_o + alpha_r ⊙ B_r. Groups are one output row by 128
  * consecutive inputs (b = k / 128). For each group:
- *   alpha_o = fl32(pairwise fp32 sum of |W| over the group's 128 inputs in order) / 128,
+ *   alpha_o = the fp32 value nearest the exact mean of |W| over the group's 128 inputs
+ *             (exact sum, one rounding, ties to even),
  *   B_o = sign(W) (+1 for +0, -0 and NaN), R = fl32(W - alpha_o B_o),
- *   alpha_r = fl32(pairwise sum of |R|) / 128, B_r = sign(R).
- * "Pairwise" is the balanced tree: inputs (0,1), (2,3), ... then pairs of pairs. The sign
- * planes use S1-128 (bit set iff -1), N*K/8 bytes each; alpha_o and alpha_r are fp32
- * [N, K/128] row-major (4-byte aligned). A group holding inf/NaN gets non-finite scales.
+ *   alpha_r = the fp32 value nearest the exact mean of |R| over the group, B_r = sign(R).
+ * The sign planes use S1-128 (bit set iff -1), N*K/8 bytes each; alpha_o and alpha_r are
+ * fp32 [N, K/128] row-major (4-byte aligned). A group holding NaN gets alpha = NaN; one
+ * holding inf (and no NaN) gets alpha_o = inf (its residual then holds NaN).
  * W fp32 [N, K] (16-byte aligned); N % 64 == 0, K % 128 == 0. Outputs must not overlap W
  * or each other. */
 int bl_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o, float* alpha_o,

@@ -184,8 +184,8 @@ __global__ __launch_bounds__(256) void gemm_rb_kernel(
   }
 }
 
-// Workgroups the register-blocked kernel aims for before it splits K (0: 256, one per CU).
-int g_gemm_rb_target = 0;
+// Workgroups the register-blocked kernel aims for before it splits K: one per CU.
+constexpr int64_t kGemmRbTarget = 256;
 
 template <int FM, int S = 3>
 hipError_t launch_rb(const int8_t* q, const float* gamma, int64_t M, int64_t K, const u32x4* W,
@@ -195,7 +195,7 @@ hipError_t launch_rb(const int8_t* q, const float* gamma, int64_t M, int64_t K, 
   const int MT = static_cast<int>((M + BM - 1) / BM), NT = static_cast<int>(N / 64);
   const int KT = static_cast<int>(K / 64);
   const int64_t tiles = static_cast<int64_t>(MT) * NT;
-  const int64_t target = g_gemm_rb_target ? g_gemm_rb_target : 256;
+  const int64_t target = kGemmRbTarget;
   int nsplit = static_cast<int>(std::min<int64_t>((target + tiles - 1) / tiles, std::max(1, KT / 8)));
   nsplit = std::max(nsplit, 1);
   if (M * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;

@@ -134,19 +134,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // workgroup's K range: loads past the range return zero without a memory access, so the
 // stream is issued ahead unconditionally (no clamped re-reads at the end of a range).
 // The integer results are identical to bl_quant_act_int8 followed by the GEMV.
-#ifndef BL_GEMVF_BATCH
-#define BL_GEMVF_BATCH 4
-#endif
-#ifndef BL_GEMVF_RING
-#define BL_GEMVF_RING 4
-#endif
-constexpr int kBatch = BL_GEMVF_BATCH;      // tiles per register batch
-constexpr int kRing = BL_GEMVF_RING;        // register batches per wave
+constexpr int kBatch = 4;                   // tiles per register batch
+constexpr int kRing = 4;                    // register batches per wave
 constexpr int kChunk = 64;                  // tiles whose planes sit in LDS at once
-#ifndef BL_GEMVF_WAVES
-#define BL_GEMVF_WAVES 4
-#endif
-constexpr int kFW = BL_GEMVF_WAVES;         // waves (bands) per workgroup
+constexpr int kFW = 4;                      // waves (bands) per workgroup
 
 constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chunk
 static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
@@ -349,7 +340,6 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
 }
 
 // Split plan of the fused kernel: workgroups own four bands each.
-int64_t g_gemvf_wg_target = 0;   // 0: by shape; changed only by tuning harnesses
 
 struct GemvFusedPlan { int64_t groups, nsplit, tps; };
 
@@ -359,7 +349,7 @@ GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
   const int64_t KT = K / 64;
   // measured on MI355X: narrow outputs do best with fewer, longer workgroups (every
   // workgroup reads the whole row for gamma), wide ones with more
-  const int64_t target = g_gemvf_wg_target ? g_gemvf_wg_target : (bands < 512 ? 256 : 512);
+  const int64_t target = bands < 512 ? 256 : 512;
   int64_t nsplit = target / groups;   // never above the target: a partial extra wave of
                                       // workgroups would run after all the others
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kBatch));
@@ -374,14 +364,13 @@ struct GemvPlan { int64_t nsplit, tps; };
 
 // Workgroups the split-K plan aims for (0: by shape). Only tuning harnesses that compile
 // this file directly change it.
-int64_t g_gemv_wg_target = 0;
 
 GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
   const int64_t bands = N / 64;
   const int64_t KT = K / 64;
   // Split K so the launch has about `target` workgroups (measured on MI355X: ~512 suit
   // narrow outputs, ~1024 wide ones), keeping at least 8 tiles (2 per wave) per workgroup.
-  const int64_t target = g_gemv_wg_target ? g_gemv_wg_target : (bands < 256 ? 512 : 1024);
+  const int64_t target = bands < 256 ? 512 : 1024;
   int64_t nsplit = (target + bands / 2) / bands;
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
   nsplit = std::max<int64_t>(nsplit, 1);
@@ -431,8 +420,7 @@ hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wp
       if (gl <= 2) BL_GEMVF_LAUNCH(1, 2);
       else if (gl <= 4) BL_GEMVF_LAUNCH(1, 4);
       else if (gl <= 8) BL_GEMVF_LAUNCH(1, 8);
-      else if (gl <= 16) BL_GEMVF_LAUNCH(1, 16);
-      else BL_GEMVF_LAUNCH(1, 0);
+      else BL_GEMVF_LAUNCH(1, 16);   // the entry point takes K <= 28672: gl <= 14
       break;
     case 2:
       if (gl <= 2) BL_GEMVF_LAUNCH(2, 2);

@@ -49,14 +49,8 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit elements
 // q of a workgroup's whole K range sits in LDS: at most kMaxTiles(MR) tiles (48 KiB).
 template <int MR>
 constexpr int mfd_max_tiles() { return 48 * 1024 / (MR * 64); }
-#ifndef BL_MFD_XR
-#define BL_MFD_XR 2
-#endif
-#ifndef BL_MFD_PRE
-#define BL_MFD_PRE 1
-#endif
-constexpr int kXR = BL_MFD_XR;     // quantisation steps whose x is loaded before the weights
-constexpr int kPre = BL_MFD_PRE;   // weight batches issued before gamma is folded
+constexpr int kXR = 2;     // quantisation steps whose x is loaded before the weights
+constexpr int kPre = 1;    // weight batches issued before gamma is folded
 
 template <int MR, int GL>
 __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(

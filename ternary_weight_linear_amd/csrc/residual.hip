@@ -6,12 +6,14 @@
 // tile, each group carrying two fp32 scales, and the two sign planes use the S1-128 layout
 // of the OneBit path.
 //
-// Packing (offline): alpha is the group's mean magnitude, formed in fp32 as a balanced
-// pairwise sum in input order times 1/128. A wave holds one group with inputs 2l, 2l+1 in
-// lane l: the lane adds its pair, then a butterfly over lanes 1, 2, 4, ..., 32 apart adds
-// pairs of pairs, which is exactly that tree (fp32 addition is commutative, so every lane
-// ends with the same bits). The residual R = W -+ alpha_o is one fp32 rounding, and the
-// lanes' sign bits are gathered into the row's four S1-128 words with two ballots per plane.
+// Packing (offline): alpha is the group's mean magnitude, the fp32 value nearest the exact
+// mean (one rounding, ties to even; no summation order enters the result). A wave holds one
+// group with inputs 2l, 2l+1 in lane l. Each magnitude m * 2^(e-150) (integer m < 2^24) is
+// the integer m << (e-1) in units of 2^-149; its pieces in 32-bit limbs at fixed bit
+// positions are summed over the wave in 64-bit integers (exact: 128 pieces < 2^32), the
+// carries are propagated, and the 288-bit total times 2^-156 (the division by 128) is
+// rounded once. The residual R = W -+ alpha_o is one fp32 rounding, and the lanes' sign
+// bits are gathered into the row's four S1-128 words with two ballots per plane.
 //
 // Forward: y[m, n] = sum_b alpha_o[n, b] (x_b . B_o[n, b]) + alpha_r[n, b] (x_b . B_r[n, b]).
 // Both group dot products run on fp16 matrix cores with B = +-1.0 built from the packed
@@ -25,10 +27,68 @@
 namespace bl {
 namespace {
 
-__device__ __forceinline__ float wave_pair_tree_sum(float v) {
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off);
+    v += (static_cast<uint64_t>(hi) << 32) | lo;
+  }
   return v;
+}
+
+// Position of |v| as an integer in units of 2^-149: limb index (32-bit limbs) and the
+// significand shifted within its limb (< 2^55, spilling into the next limb).
+__device__ __forceinline__ void abs_units(float v, int& limb, uint64_t& shifted) {
+  const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  const int e = static_cast<int>(u >> 23);
+  const uint32_t m = e ? ((u & 0x7FFFFFu) | 0x800000u) : u;
+  const int p = (e ? e : 1) - 1;
+  limb = p >> 5;
+  shifted = static_cast<uint64_t>(m) << (p & 31);
+}
+
+// The fp32 value nearest the exact mean of |a|, |b| over the wave's 128 values (ties to
+// even). NaN anywhere gives NaN, else inf anywhere gives inf. Every lane returns the result.
+__device__ float group_abs_mean_exact(float a, float b) {
+  const uint32_t ua = __float_as_uint(a) & 0x7FFFFFFFu, ub = __float_as_uint(b) & 0x7FFFFFFFu;
+  if (__builtin_amdgcn_ballot_w64(ua > 0x7F800000u || ub > 0x7F800000u))
+    return __uint_as_float(0x7FC00000u);
+  if (__builtin_amdgcn_ballot_w64(ua == 0x7F800000u || ub == 0x7F800000u))
+    return __uint_as_float(0x7F800000u);
+  int la, lb;
+  uint64_t va, vb;
+  abs_units(a, la, va);
+  abs_units(b, lb, vb);
+  constexpr int L = 9;                               // 288 bits > 2^7 * 2^277
+  uint32_t A[L];
+  uint64_t carry = 0;
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    uint64_t c = (la == j ? (va & 0xFFFFFFFFu) : 0u) + (la + 1 == j ? (va >> 32) : 0u) +
+                 (lb == j ? (vb & 0xFFFFFFFFu) : 0u) + (lb + 1 == j ? (vb >> 32) : 0u);
+    c = wave_sum_u64(c) + carry;
+    A[j] = static_cast<uint32_t>(c);
+    carry = c >> 32;
+  }
+  // mean = A * 2^-156. Keep 24 significant bits (never finer than the subnormal spacing
+  // 2^-149 = 2^7 units), round half to even on the dropped bits.
+  int top = -1;
+#pragma unroll
+  for (int j = L - 1; j >= 0; --j)
+    if (top < 0 && A[j]) top = 32 * j + 31 - __builtin_clz(A[j]);
+  if (top < 0) return 0.0f;
+  const int shift = top - 23 > 7 ? top - 23 : 7;
+  auto bit = [&](int pos) -> uint32_t { return (A[pos >> 5] >> (pos & 31)) & 1u; };
+  uint32_t mant = 0;
+  for (int i = 0; i < 24 && shift + i <= top; ++i) mant |= bit(shift + i) << i;
+  const uint32_t half = bit(shift - 1);
+  bool below = false;
+  for (int i = 0; i < shift - 1 && !below; ++i) below = bit(i) != 0;
+  if (half && (below || (mant & 1u))) ++mant;
+  // value = mant * 2^(shift - 156); for shift = 7 and mant < 2^23 this is the subnormal
+  // encoding, otherwise the biased exponent is shift - 6 (a carry to 2^24 bumps it).
+  return __uint_as_float((static_cast<uint32_t>(shift - 7) << 23) + mant);
 }
 
 // Lane l of the packing wave holds tile inputs 2l, 2l + 1, i.e. c = 32s + 8g + 2q + e with
@@ -53,11 +113,11 @@ __global__ __launch_bounds__(256) void residual_pack_kernel(
   if (item >= N * KB) return;                           // whole waves leave together
   const int64_t n = item / KB, b = item % KB;
   const float2 w = reinterpret_cast<const float2*>(W + n * K + b * 128)[lane];
-  const float ao = wave_pair_tree_sum(fabsf(w.x) + fabsf(w.y)) * (1.0f / 128.0f);
+  const float ao = group_abs_mean_exact(w.x, w.y);
   const bool n0 = w.x < 0.0f, n1 = w.y < 0.0f;
   const float r0 = w.x - (n0 ? -ao : ao);
   const float r1 = w.y - (n1 ? -ao : ao);
-  const float ar = wave_pair_tree_sum(fabsf(r0) + fabsf(r1)) * (1.0f / 128.0f);
+  const float ar = group_abs_mean_exact(r0, r1);
   const uint64_t bo_e = __builtin_amdgcn_ballot_w64(n0), bo_o = __builtin_amdgcn_ballot_w64(n1);
   const uint64_t br_e = __builtin_amdgcn_ballot_w64(r0 < 0.0f);
   const uint64_t br_o = __builtin_amdgcn_ballot_w64(r1 < 0.0f);

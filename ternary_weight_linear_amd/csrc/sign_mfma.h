@@ -159,13 +159,9 @@ __device__ __forceinline__ void sign_compute_tile(const SignTile<RES>& T, sm_f32
   }
 }
 
-// Tile sets per wave: sign_depth() - 1 tiles in flight while one is multiplied. Tuning
-// harnesses that compile the sources directly may override it.
-#ifndef BL_SIGN_DEPTH
-#define BL_SIGN_DEPTH 3
-#endif
+// Tile sets per wave: sign_depth() - 1 tiles in flight while one is multiplied.
 template <bool RES>
-constexpr int sign_depth() { return BL_SIGN_DEPTH; }
+constexpr int sign_depth() { return 3; }
 
 template <bool RES>
 __global__ __launch_bounds__(256) void sign_mfma_kernel(const SignMfmaArgs a) {
@@ -276,8 +272,7 @@ struct SignPlan { int64_t bands, mtiles, nsplit, tps; };
 // Workgroups to aim for. Tuning harnesses that compile the sources directly may set it
 // (0 = the default); the workspace is sized for the default.
 constexpr int64_t kSignWgTarget = 256;
-inline int64_t g_sign_wg_target = 0;
-inline int64_t sign_wg_target() { return g_sign_wg_target > 0 ? g_sign_wg_target : kSignWgTarget; }
+inline int64_t sign_wg_target() { return kSignWgTarget; }
 
 // Splits K across workgroups only while bands x x-tiles leaves the chip short of `target`
 // workgroups; each split keeps at least one tile per wave.

@@ -30,6 +30,7 @@
 // the fp16 bit patterns with the sign cleared; >= 0x7C00 flags NaN/inf), q = rne(127 x /
 // gamma) clipped to +-127 in fp32, eight wave ballots make a tile's bit planes, and per
 // 32-input word and plane one select and one popcount; acc = sum_b c_b A_b + popcount(N).
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -54,27 +55,18 @@ __device__ __forceinline__ BL_GLOBAL T* gptr_mut(T* p) {
   return (BL_GLOBAL T*)(p);
 }
 
-#ifndef BL_STACK_BATCH
-#define BL_STACK_BATCH 4
-#endif
-#ifndef BL_STACK_CONTRIB
-#define BL_STACK_CONTRIB 254
-#endif
 // One workgroup of 8 waves per CU (measured on MI355X, 70B-shaped pass at M = 1: 5.74 ms
 // against 6.18 ms with three 4-wave workgroups per CU; 16 waves, 5.65 ms, leave too few
 // registers for M = 3, 4). The waves of a workgroup meet at every chunk barrier, so no lone
 // late workgroup is left on a CU at the end of a linear.
 constexpr int kSW = 8;                    // waves per workgroup, one 64-row band each
-constexpr int kSB = BL_STACK_BATCH;       // tiles per register batch; the ring holds two
+constexpr int kSB = 4;                    // tiles per register batch; the ring holds two
 constexpr int kSChunk = 64;               // tiles whose planes sit in LDS at once
 constexpr int kSPerWave = kSChunk / kSW;  // tiles each wave quantises per chunk
-#ifndef BL_STACK_GX
-#define BL_STACK_GX 4
-#endif
-constexpr int kSGX = BL_STACK_GX;         // 16-byte x loads per thread per gamma round
+constexpr int kSGX = 4;                   // 16-byte x loads per thread per gamma round
 // Workgroups sharing one group at most (<= kMaxIntSplits - 1 so a split word never
 // overflows its count).
-constexpr int64_t kSMaxContrib = BL_STACK_CONTRIB;
+constexpr int64_t kSMaxContrib = 254;
 static_assert(kSMaxContrib <= kMaxIntSplits - 1, "split word count");
 constexpr uint32_t kStackMagic = 0x4B435453u;
 // Bound of one grid-wide wait: 2 s of the 100 MHz real-time counter.
@@ -546,11 +538,13 @@ hipError_t launch_stack_mr(const void* plan, int count, uint32_t* bar, uint64_t*
                            hipStream_t s) {
   // persistent grid: every workgroup must be resident at once (cooperative launch); one per
   // CU, or BL_STACK_GRID workgroups if that is set and smaller
-  static int cached[64] = {};
+  // grid per device, computed once; calling threads may race to fill a slot, and every one
+  // of them computes the same value, so relaxed atomics suffice
+  static std::atomic<int> cached[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int grid = (dev >= 0 && dev < 64) ? cached[dev] : 0;
+  int grid = (dev >= 0 && dev < 64) ? cached[dev].load(std::memory_order_relaxed) : 0;
   if (grid == 0) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -560,7 +554,7 @@ hipError_t launch_stack_mr(const void* plan, int count, uint32_t* bar, uint64_t*
     if (e != hipSuccess) return e;
     if (per_cu < 1 || cus < 1) return hipErrorCooperativeLaunchTooLarge;
     grid = cus;   // per_cu >= 1: one workgroup per CU is resident
-    if (dev >= 0 && dev < 64) cached[dev] = grid;
+    if (dev >= 0 && dev < 64) cached[dev].store(grid, std::memory_order_relaxed);
   }
   grid = std::min(grid, kMaxStackGrid);
   if (const char* env = std::getenv("BL_STACK_GRID")) {

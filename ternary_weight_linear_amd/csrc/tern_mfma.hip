@@ -30,10 +30,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef BL_TERN_DEPTH
-#define BL_TERN_DEPTH 2
-#endif
-constexpr int kTernDepth = BL_TERN_DEPTH;   // tile sets per wave (depth - 1 in flight)
+constexpr int kTernDepth = 2;   // tile sets per wave (depth - 1 in flight)
 
 __device__ __forceinline__ uint32_t tern_expand(uint32_t pb, uint32_t nb) {
   // pb + 255 nb per byte as (pb - nb) + (nb << 8) (exact modulo 2^32: the borrows cancel);
@@ -240,10 +237,7 @@ __global__ __launch_bounds__(256) void tern_mfma_kernel(const TernArgs a) {
 // tiles stays below the split words' 2^23 bias as long as a split spans at most
 // kMfMaxSplitTiles tiles; unshifted, 16 * 254 * K and 64 * 127 * K stay below 2^31 for
 // K <= 65536.
-#ifndef BL_MF_DEPTH
-#define BL_MF_DEPTH 3
-#endif
-constexpr int kMfDepth = BL_MF_DEPTH;
+constexpr int kMfDepth = 3;
 constexpr int kMfMaxSplitTiles = ((1 << 23) - 1) / (254 * 64);   // 516
 
 template <int FM>
@@ -544,12 +538,6 @@ struct TernPlan { int64_t bands, mgroups, nsplit, tps; int fm; bool split; };
 
 }  // namespace
 
-// Tuning knobs (harnesses that compile this file directly): workgroups to aim for, and a
-// fixed q rows per wave (16 FM); 0 = by shape.
-int64_t g_tern_wg_target = 0;
-int g_tern_fm = 0;
-int g_tern_split = -1;     // -1 by rows, 0 expand, 1 split
-
 namespace {
 
 TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
@@ -557,26 +545,20 @@ TernPlan plan_tern(int64_t M, int64_t N, int64_t K) {
   // measured on MI355X (70B-shaped decode at M = 8..64): one 16-row tile of q per wave
   // (more workgroups, each weight tile re-read per 16 rows from L2) except for very wide
   // outputs, where two
-  const int fm = g_tern_fm > 0 ? g_tern_fm : (M > 16 && bands >= 512 ? 2 : 1);
+  const int fm = M > 16 && bands >= 512 ? 2 : 1;
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
-  const int64_t target = g_tern_wg_target > 0 ? g_tern_wg_target : 512;
+  const int64_t target = 512;
   int64_t nsplit = (target + bands * mgroups - 1) / (bands * mgroups);
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));   // >= 2 tiles per wave
   nsplit = std::max<int64_t>(nsplit, 1);
   if (M * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
   nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
   const int64_t tps = (KT + nsplit - 1) / nsplit;
-  const bool split = g_tern_split >= 0 ? g_tern_split == 1 : fm <= 2;   // VALU-bound at few rows
+  const bool split = fm <= 2;   // VALU-bound at few rows
   return {bands, mgroups, (KT + tps - 1) / tps, tps, fm, split};
 }
 
 }  // namespace
-
-// Tuning knobs (harnesses that compile this file directly): workgroups the T2-MF64 kernels
-// aim for (0: by kernel) and the kernel (0: by shape, 1: q staged in LDS, 2: per band).
-int64_t g_mf_wg_target = 0;
-int g_mf_kernel = 0;
-int g_mf_fm = 0;   // 16-row tiles of q per workgroup of the staged-q kernel (0: by M)
 
 namespace {
 
@@ -594,7 +576,7 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
                           hipStream_t s) {
   const int64_t KT = K / 64, bands = N / 64;
   const int64_t mgroups = (M + 15) / 16;
-  const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 512;
+  const int64_t target = 512;
   int64_t nsplit = (target + bands * mgroups - 1) / (bands * mgroups);
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 8));
   nsplit = std::max<int64_t>(nsplit, (KT + kMfMaxSplitTiles - 1) / kMfMaxSplitTiles);
@@ -615,7 +597,6 @@ hipError_t launch_mf_band(const int8_t* q, const float* gamma, const int32_t* ro
 // still gives >= 192 workgroups (the decoded weights serve more rows), else 16 (row groups
 // of a band group share its weights through one XCD's L2, and more workgroups win).
 int mfq_fm(int64_t M, int64_t groups) {
-  if (g_mf_fm > 0) return g_mf_fm > 2 ? 3 : g_mf_fm;
   // measured on MI355X: 48-row tiles for prefill-sized M over >= 32 band groups (3B at
   // M = 512: gate|up 34.2 vs 46.3 us with 16-row tiles, q|k|v 26.8 vs 28.0 us; o and down,
   // 13 groups, too few work items, were slower; 64-row tiles were slower everywhere),
@@ -634,7 +615,7 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
   // K is split until about `target` workgroups; a split spans whole ring turns where the
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
-  const int64_t target = g_mf_wg_target > 0 ? g_mf_wg_target : 256;
+  const int64_t target = 256;
   int64_t nsplit = std::max<int64_t>(1, target / (groups * mgroups));
   const int64_t turn = kQC * kQRing;
   int64_t tps = (KT + nsplit - 1) / nsplit;
@@ -667,7 +648,7 @@ hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* ro
   // split-word atomics per split, more than the per-band kernel's repeated weight reads
   const int64_t groups = (N / 64 + 3) / 4;
   const int64_t items = groups * ((M + 16 * mfq_fm(M, groups) - 1) / (16 * mfq_fm(M, groups)));
-  const bool quad = g_mf_kernel == 1 || (g_mf_kernel == 0 && items >= 160);
+  const bool quad = items >= 160;
   return quad ? launch_mf_quad(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,
                                ws_acc, s)
               : launch_mf_band(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,

@@ -43,3 +43,28 @@ def assert_scaled(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, tol: 
         raise AssertionError(f"{bad.sum()} elements out of tolerance, first at {tuple(i)}: "
                              f"gpu={y_gpu[tuple(i)]!r} ref={y_ref[tuple(i)]!r} scale={scale[tuple(i)]!r}")
     return float((err / scale).max())
+
+
+def gamma_ladder() -> np.ndarray:
+    """fp16 row maxima for the exhaustive quantiser sweeps (>= 64 values): every power of two
+    of a spread of binades with its neighbours one ulp below and above (the subnormal range
+    included, where an ulp is 2^-24), the largest subnormal and the extremes, and mantissas
+    spread over [1, 2) in a few binades. Sorted and unique."""
+    vals = []
+    for p in (-24, -23, -20, -17, -15, -14, -13, -10, -7, -4, -1, 0, 1, 2, 3, 4, 6, 7, 8, 10,
+              12, 14, 15):
+        b = np.float16(2.0 ** p)
+        vals += [b, np.nextafter(b, np.float16(0)), np.nextafter(b, np.float16(np.inf))]
+    vals += [np.float16(v) for v in (65504, 127.0, 3.14, 0.0999, 6.1e-5, 1023 * 2.0 ** -24,
+                                     1.5 * 2.0 ** -14, 100.0, 1.0 / 3.0, 7.7, 254.0, 1e4)]
+    for e, j in ((-9, 3), (-2, 11), (0, 19), (5, 27), (9, 31), (13, 7), (1, 1021), (-6, 513)):
+        vals.append(np.float16((1 + j / 1024) * 2.0 ** e))
+    v = np.unique(np.array([x for x in vals if x > 0], dtype=np.float16))
+    assert v.size >= 64
+    return v
+
+
+def finite_fp16() -> np.ndarray:
+    """Every finite fp16 value (63,488 of them, both zeros included)."""
+    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    return all16[np.isfinite(all16)]

@@ -1,12 +1,21 @@
-"""Full-size parity in the launch configuration the benchmark times.
+"""Full-size parity for the 70B-shaped stack (80 layers x q 8192x8192, k/v 1024x8192,
+o 8192x8192, gate/up 28672x8192, down 8192x28672), in the launch configurations the
+benchmark times.
 
-One layer of the 70B-shaped stack is built exactly as bench.py builds it (GPU counter-based
-codes, packed into stacked q|k|v and gate|up buffers, repacked into T2-MF64) and run through
-the same entry points (the fused quantise + add-only GEMV at M = 1, the benchmark's default
-pass; the fused T2-MF64 matrix-core decode at M = 1, 2, its comparison line; quantiser +
-int8-MFMA products at M = 8 and 64). Sampled output rows are recomputed by the oracle from
-codes regenerated on the host. Graph-replayed passes are checked bit-for-bit against eager
-launches over several replays."""
+The stack is built exactly as bench.py builds it (GPU counter-based codes, packed into
+stacked q|k|v and gate|up T2-PN-64 buffers, repacked into T2-MF64 where the matrix-core
+lines need it). The checks follow the stack's parity budget:
+
+* layers 0 and 79 in full: every row of all seven matrices at M = 1, 8, 32 and 64, the
+  int32 accumulators bit-exact against the oracle (acc-returning entry points on the same
+  weights) and the fp32 outputs of the benchmark's own launches within 1e-3 of the oracle
+  on every element;
+* every layer: 128 seeded rows per matrix at M = 1, 8, 32 and 64 through a graph-replayed
+  pass of the benchmark's launches, int32 and fp32 as above;
+* the persistent whole-stack launch, graph replays against eager launches.
+
+The oracle regenerates every code it uses on the host (synth.ternary_codes, the host twin
+of the GPU generator)."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +24,7 @@ import oracle
 import synth
 import synth.gpu as sgpu
 import ternary_weight_linear_amd as tw
-from tests.gpu_util import DEV, assert_rel, host, say
+from tests.gpu_util import DEV, assert_rel, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -61,25 +70,143 @@ def _sampled_reference(x16, parts, K, rows_per_member, seed):
 
 
 @pytest.fixture(scope="module")
-def layer0():
-    say("fullsize: building layer 0 of the 70B-shaped stack")
-    return _layer(0)
+def stack70b():
+    say("fullsize: building the 80-layer 70B-shaped stack (17.1 GB)")
+    layers = []
+    for layer in range(synth.LLAMA70B_LAYERS):
+        layers.append(_layer(layer))
+        if layer % 20 == 19:
+            say("fullsize: built", layer + 1, "layers")
+    return layers
 
 
-@pytest.mark.parametrize("M", [1, 8, 64])
-def test_stack_layer_sampled_rows(layer0, M):
+@pytest.fixture(scope="module")
+def layer0(stack70b):
+    return stack70b[0]
+
+
+BENCH_M = [1, 8, 32, 64]
+ACC_CHUNK = 4096            # oracle rows per fp64 product (bounds host memory)
+
+
+def _bench_x(layer, gi, M):
+    """The benchmark's activations for (layer, group) at M tokens."""
+    return synth.normal_fp16((M, K_OF[gi]), 0, 5, 1000 + layer, gi)
+
+
+K_OF = [SHAPES[members[0]][1] for _, members in GROUPS]
+
+
+def _gpu_bench_launch(x, buf, wmf, beta, N, M, out=None):
+    """The launch the benchmark times for one group: the fused quantise + add-only GEMV at
+    M <= 2 (T2-PN-64), bl_bitlinear_forward_mf (T2-MF64) above."""
+    if M <= 2:
+        return tw.bl_bitlinear_forward(x, buf, beta, N, path=tw.BL_PATH_GEMV, out=out)
+    return tw.bl_bitlinear_forward_mf(x, wmf, beta, N, out=out)
+
+
+def _gpu_acc(x, buf, wmf, N, K, M):
+    """int32 accumulators for the same weights from an acc-returning entry point: the
+    add-only GEMV (X8-64 planes) at M <= 2, the T2-MF64 matrix-core product above; the
+    quantiser's outputs are returned for the bit-exact check."""
+    q, gamma, rowsum, planes = tw.bl_quant_act_int8(x, want_planes=M <= 2)
+    if M <= 2:
+        acc = tw.bl_bitlinear_acc_i32(buf, N, K, planes=planes, path=tw.BL_PATH_GEMV)
+    else:
+        _, acc = tw.bl_bitlinear_gemm_mf(q, gamma, rowsum, wmf, None, N, want_y=False, want_acc=True)
+    return acc, q, gamma, rowsum
+
+
+@pytest.mark.parametrize("layer", [0, 79])
+@pytest.mark.parametrize("gi", [0, 1, 2, 3])
+def test_full_layer_every_row(stack70b, layer, gi):
+    """Every row of the group's matrices, M = 1, 8, 32, 64: q, gamma and row sums bit-exact,
+    int32 accumulators bit-exact (and the T2-PN-64 matrix-core product's too), fp32 outputs
+    of the benchmark's launch within 1e-3 everywhere."""
+    gname, buf, N, K, parts = stack70b[layer][gi]
     beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
-    for gi, (gname, buf, N, K, parts) in enumerate(layer0):
-        say("fullsize", gname, "M", M, "N", N, "K", K)
-        x16 = synth.normal_fp16((M, K), 0, 5, 1000, gi)
-        x = torch.from_numpy(x16).to(DEV)
-        if M <= 2:
-            y = tw.bl_bitlinear_forward(x, buf, beta, N, path=tw.BL_PATH_GEMV)
-        else:
-            q, gamma, _, _ = tw.bl_quant_act_int8(x, want_rowsum=False, want_planes=False)
-            y = tw.bl_bitlinear_gemm(q, gamma, buf, beta, N)
-        ids, yref = _sampled_reference(x16, parts, K, 48, seed=gi + 10 * M)
-        assert_rel(host(y)[:, ids], yref)
+    say("fullsize every row: layer", layer, gname, N, "x", K, "(host codes)")
+    codes = np.concatenate([synth.ternary_codes(key, Nm, K) for _, key, Nm, _ in parts])
+    xs = {M: _bench_x(layer, gi, M) for M in BENCH_M}
+    qs = {M: oracle.quant_act_int8(xs[M]) for M in BENCH_M}
+    qall = np.concatenate([qs[M][0] for M in BENCH_M])
+    ref_all = np.concatenate([oracle.acc_exact(qall, codes[r:r + ACC_CHUNK])
+                              for r in range(0, N, ACC_CHUNK)], axis=1)
+    del codes
+    wmf = tw.bl_repack_ternary_mf(buf, N, K)
+    r0 = 0
+    for M in BENCH_M:
+        say("fullsize every row: layer", layer, gname, "M", M)
+        rq, rg, rrow = qs[M]
+        ref_acc = ref_all[r0:r0 + M]
+        r0 += M
+        x = dev(xs[M])
+        acc, q, gamma, rowsum = _gpu_acc(x, buf, wmf, N, K, M)
+        assert np.array_equal(host(q), rq) and np.array_equal(host(rowsum), rrow)
+        assert np.array_equal(host(gamma).view(np.uint32), rg.view(np.uint32))
+        assert np.array_equal(host(acc), ref_acc), f"int32 accumulators, M = {M}"
+        if M > 2:
+            acc_pn = tw.bl_bitlinear_acc_i32(buf, N, K, q=q, path=tw.BL_PATH_GEMM)
+            assert np.array_equal(host(acc_pn), ref_acc), f"T2-PN-64 product, M = {M}"
+        y = _gpu_bench_launch(x, buf, wmf, beta, N, M)
+        assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, synth.BETA_DIRECT))
+    del wmf
+
+
+_SAMPLED = {}
+
+
+def _sampled_codes(layer, parts, K):
+    """128 seeded rows of every matrix of a group: (stacked row ids, host codes)."""
+    key0 = (layer, parts[0][0])
+    if key0 not in _SAMPLED:
+        ids, cs = [], []
+        for name, key, N, first in parts:
+            rows = np.sort(synth.rng(0, 8, layer, MIDS[name]).choice(N, size=min(128, N), replace=False))
+            cs.append(synth.ternary_codes(key, N, K, rows=rows))
+            ids.append(first + rows)
+        _SAMPLED[key0] = (np.concatenate(ids), np.concatenate(cs))
+    return _SAMPLED[key0]
+
+
+@pytest.mark.parametrize("M", BENCH_M)
+def test_all_layers_sampled_rows(stack70b, M):
+    """All 80 layers through one graph-replayed pass of the benchmark's launches (the
+    configuration it times), then 128 seeded rows of every matrix: int32 accumulators
+    bit-exact and fp32 outputs within 1e-3 of the oracle."""
+    beta = torch.tensor([float(synth.BETA_DIRECT)], dtype=torch.float32, device=DEV)
+    items = []
+    for layer, lg in enumerate(stack70b):
+        for gi, (gname, buf, N, K, parts) in enumerate(lg):
+            x16 = _bench_x(layer, gi, M)
+            wmf = tw.bl_repack_ternary_mf(buf, N, K) if M > 2 else None
+            y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+            items.append((layer, gi, x16, dev(x16), buf, wmf, N, K, parts, y))
+    say("fullsize all layers M", M, "launches", len(items))
+
+    def run():
+        for layer, gi, x16, x, buf, wmf, N, K, parts, y in items:
+            _gpu_bench_launch(x, buf, wmf, beta, N, M, out=y)
+
+    run()                                   # allocates the workspace outside the capture
+    torch.cuda.synchronize()
+    for it in items:
+        it[-1].fill_(float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    for layer, gi, x16, x, buf, wmf, N, K, parts, y in items:
+        if gi == 0 and layer % 16 == 0:
+            say("fullsize all layers M", M, "checking layer", layer)
+        ids, codes = _sampled_codes(layer, parts, K)
+        rq, rg, _ = oracle.quant_act_int8(x16)
+        ref_acc = oracle.acc_exact(rq, codes)
+        acc, _, _, _ = _gpu_acc(x, buf, wmf, N, K, M)
+        assert np.array_equal(host(acc)[:, ids], ref_acc), (layer, gi, M)
+        assert_rel(host(y)[:, ids], oracle.bitlinear_output(ref_acc, rg, synth.BETA_DIRECT))
+    del g, items
 
 
 def test_stack_layer_graph_replays_match_eager(layer0):

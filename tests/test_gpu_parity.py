@@ -12,7 +12,8 @@ import oracle
 import synth
 import synth.gpu as sgpu
 import ternary_weight_linear_amd as tw
-from tests.gpu_util import DEV, assert_rel, assert_scaled, dev, host, say
+from tests.gpu_util import (DEV, assert_rel, assert_scaled, dev, finite_fp16, gamma_ladder,
+                            host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,18 +135,28 @@ def test_quant_act_degenerate_rows():
     _quant_case(x)
 
 
-def test_quant_act_exhaustive_fp16():
-    """Every finite fp16 x against a ladder of gamma values: rows [x, gamma, 0, ...]."""
-    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
-    finite = all16[np.isfinite(all16)]
-    for gamma in [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
-                  np.float16(3.14), np.float16(127.0)]:
+def ladder_rows(K):
+    """Rows [x_0 .. x_{K-2}, gamma]: for every gamma of the ladder, every finite fp16 x with
+    |x| <= gamma, K - 1 per row (the last row of a gamma zero-padded), so that each row's
+    maximum is its gamma. Returns fp16 [R, K]."""
+    finite = finite_fp16()
+    rows = []
+    for gamma in gamma_ladder():
         xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
-        say("quant exhaustive gamma", gamma, xs.size)
-        x = np.zeros((xs.size, 64), np.float16)
-        x[:, 0] = xs
-        x[:, 1] = gamma
-        _quant_case(x)
+        for i in range(0, xs.size, K - 1):
+            r = np.zeros(K, np.float16)
+            r[:min(K - 1, xs.size - i)] = xs[i:i + K - 1]
+            r[K - 1] = gamma
+            rows.append(r)
+    return np.stack(rows)
+
+
+def test_quant_act_exhaustive_fp16():
+    """Every finite fp16 x against every gamma of the ladder (84 values: subnormal gammas,
+    powers of two and their one-ulp neighbours, spread mantissas), both kernels."""
+    x = ladder_rows(64)
+    say("quant exhaustive", x.shape)
+    _quant_case(x)
 
 
 # ----------------------------------------------------------------------------- products
@@ -241,6 +252,49 @@ def test_forward_fused_gemv_exact_integers():
     assert np.all(np.isnan(y[2]))
 
 
+# The 7B-shaped decode linears (stacked q|k|v 12288 x 4096, stacked gate|up 22016 x 4096,
+# down 4096 x 11008) and row lengths that select each of the fused kernel's row-load
+# variants: 2 / 4 / 8 / 16 loads per thread (K <= 4096 / 8192 / 16384 / 28672 at M = 1,
+# the longest row the entry point takes) and, at M = 2, the loop past 16384.
+@pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (2, 12288, 4096), (1, 22016, 4096),
+                                   (2, 22016, 4096), (1, 4096, 11008), (2, 4096, 11008),
+                                   (1, 128, 16384), (2, 192, 16384), (2, 64, 16448),
+                                   (1, 256, 16448), (1, 256, 28672), (2, 128, 28672)])
+def test_forward_fused_gemv_shapes(M, N, K):
+    """Fused quantise + add-only GEMV (the decode path of bl_bitlinear_forward): fp32 output
+    against the oracle on every element, and the int32 accumulators of the add-only kernel
+    bit-exact; the fused output is bitwise the unfused GEMV's (same integers, same
+    epilogue)."""
+    say("fused gemv shape", M, N, K)
+    codes, packed = _weights(N, K, seed=6)
+    x = synth.normal_fp16((M, K), 6, 100, M, K)
+    beta = np.float32(synth.BETA_DIRECT)
+    db = dev(np.array([beta]))
+    y = tw.bl_bitlinear_forward(dev(x), packed, db, N, path=tw.BL_PATH_GEMV)
+    rq, rg, _ = oracle.quant_act_int8(x)
+    ref_acc = oracle.acc_exact(rq, codes)
+    assert_rel(host(y), oracle.bitlinear_output(ref_acc, rg, beta))
+    q, gamma, _, planes = tw.bl_quant_act_int8(dev(x))
+    acc = tw.bl_bitlinear_acc_i32(packed, N, K, planes=planes, path=tw.BL_PATH_GEMV)
+    assert np.array_equal(host(acc), ref_acc)
+    y2 = tw.bl_bitlinear_gemv(planes, gamma, packed, db, N, K)
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+@pytest.mark.parametrize("K", [1024, 11008, 28672])
+def test_forward_fused_gemv_exact_integers_long_rows(K):
+    """As test_forward_fused_gemv_exact_integers, for the 8- and 16-load row variants."""
+    say("fused gemv integers", K)
+    N = 384
+    codes, packed = _weights(N, K, seed=7)
+    x = synth.rng(7, 6, K).integers(-127, 128, size=(2, K)).astype(np.float16)
+    x[:, 0] = 127
+    one = dev(np.array([1.0], np.float32))
+    for m in (1, 2):
+        y = host(tw.bl_bitlinear_forward(dev(x[:m]), packed, one, N, path=tw.BL_PATH_GEMV))
+        assert np.array_equal(y, oracle.acc_exact(x[:m].astype(np.int8), codes).astype(np.float32))
+
+
 def _fused_q(x, packed_eye, K):
     """Run the fused quantise + GEMV over an identity weight matrix with beta = 1, where
     y = q * fp32(gamma / 127) exactly up to one rounding, and recover q (exact: |q| <= 127)."""
@@ -252,33 +306,26 @@ def _fused_q(x, packed_eye, K):
         return y, np.rint(y.astype(np.float64) / scale[:, None])
 
 
-@pytest.mark.parametrize("M,K", [(1, 8192), (2, 8192), (3, 2048), (4, 2048)])
+@pytest.mark.parametrize("M,K", [(1, 8192), (2, 8192), (3, 2048), (4, 2048), (1, 11008),
+                                 (2, 16384), (1, 28672), (2, 28672)])
 def test_forward_fused_quantiser_exhaustive(M, K):
-    """The fused kernel quantises x itself; every finite fp16 x against a ladder of gamma
-    values (rows [x..., gamma]) must give the oracle's q to the bit, including quotients
-    that are exact half-integers (ties to even) and ones within an ulp of them."""
+    """The fused kernel quantises x itself; every finite fp16 x against every gamma of the
+    ladder (rows [x..., gamma]) must give the oracle's q to the bit, including quotients
+    that are exact half-integers (ties to even) and ones within an ulp of them. K picks the
+    kernel's row-load variant (2, 4, 8, 16 loads per thread, or the loop)."""
     eye = dev(np.eye(K, dtype=np.int8))
     packed = tw.bl_pack_ternary(eye)
     del eye
-    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
-    finite = all16[np.isfinite(all16)]
-    ladder = [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
-              np.float16(3.14), np.float16(127.0)]
-    if M > 2:
-        ladder = ladder[:3]
-    for gamma in ladder:
-        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
-        per = K - 1
-        rows = [xs[i:i + per] for i in range(0, xs.size, per)]
-        say("fused quant exhaustive", M, K, gamma, xs.size, len(rows))
-        for r0 in range(0, len(rows), M):
-            x = np.zeros((M, K), np.float16)
-            x[:, K - 1] = gamma
-            for m, chunk in enumerate(rows[r0:r0 + M]):
-                x[m, :chunk.size] = chunk
-            rq, _, _ = oracle.quant_act_int8(x)
-            _, q = _fused_q(x, packed, K)
-            assert np.array_equal(q, rq.astype(np.float64)), (gamma, r0)
+    rows = ladder_rows(K)
+    say("fused quant exhaustive", M, K, rows.shape)
+    for r0 in range(0, rows.shape[0], M):
+        x = np.zeros((M, K), np.float16)
+        chunk = rows[r0:r0 + M]
+        x[:chunk.shape[0]] = chunk
+        x[chunk.shape[0]:, K - 1] = 1.0
+        rq, _, _ = oracle.quant_act_int8(x)
+        _, q = _fused_q(x, packed, K)
+        assert np.array_equal(q, rq.astype(np.float64)), (r0, x[:, K - 1])
     # degenerate rows: all zero, one NaN, one inf, all -65504
     x = synth.normal_fp16((M, K), 0, 94, 1)
     x[0] = 0
@@ -394,6 +441,14 @@ def _residual_weight(N, K, seed=0):
     W[1, :128] = np.where(synth.rng(seed, 12, 1).random(128) < 0.5, -0.375, 0.375)
     W[2, :6] = [0.0, -0.0, -0.0, 0.0, -0.0, -0.0]
     W[3, :128] = synth.normal_fp32(128, seed, 12, 2) * np.float32(1e-39)
+    W[4, :128] = np.float32(2.0 ** -25)       # exact mean 2^-7 + 127 * 2^-32: an fp32 running
+    W[4, 0] = 1.0                             # sum (any order) absorbs the small terms
+    W[5, :128] = 1.0                          # mean 1 + 2^-24: a tie, to even (1.0)
+    W[5, 77] = np.float32(1 + 2.0 ** -17)
+    W[6, :128] = 0.0                          # mean 1.5 * 2^-149: a subnormal tie
+    W[6, 100] = np.float32(2.0 ** -149 * 192)
+    W[7, :128] = np.float32(3.4028235e38)     # 128 x FLT_MAX: the largest exact sum
+    W[7, 1::2] *= -1
     if N > 64:
         W[64, :128] = 1.0
         W[64, 5] = np.inf
@@ -410,7 +465,8 @@ def _bits_equal(a, b):
 
 @pytest.mark.parametrize("N,K", [(64, 128), (192, 384), (512, 1024), (4096, 4096)])
 def test_residual_binarize(N, K):
-    """Sign planes bit-exact; both scales bit-exact (same fp32 pairwise order)."""
+    """Sign planes bit-exact; both scales bit-exact (each the fp32 value nearest the exact
+    group mean, so no summation order is shared with the oracle)."""
     say("residual_binarize", N, K)
     W = _residual_weight(N, K)
     po, ao, pr, ar = tw.bl_residual_binarize(dev(W))
@@ -420,6 +476,8 @@ def test_residual_binarize(N, K):
     assert _bits_equal(host(ao), ao_ref)
     assert _bits_equal(host(ar), ar_ref)
     assert ao_ref[0, 0] == 0 and ar_ref[1, 0] == 0 and 0 < ao_ref[3, 0] < np.float32(1e-38)
+    assert ao_ref[4, 0] == np.float32(2.0 ** -7 + 128 * 2.0 ** -32) and ao_ref[5, 0] == 1.0
+    assert ao_ref[6, 0] == np.float32(2 * 2.0 ** -149) and ao_ref[7, 0] == np.float32(3.4028235e38)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 4096, 4096), (2, 320, 384), (3, 192, 1280),
@@ -551,6 +609,35 @@ def test_stack_small_grids(grid, monkeypatch):
         assert_rel(host(l["y"]), _stack_oracle(l))
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_stack_quantiser_exhaustive(M):
+    """The persistent launch quantises every linear's x itself: one linear per M rows of
+    the gamma-ladder sweep (every finite fp16 x against every gamma, identity weights,
+    beta = 1), q recovered from y and compared with the oracle's to the bit."""
+    K = 2048
+    packed = tw.bl_pack_ternary(dev(np.eye(K, dtype=np.int8)))
+    one = dev(np.array([1.0], np.float32))
+    rows = ladder_rows(K)
+    xs, lins = [], []
+    for r0 in range(0, rows.shape[0], M):
+        x = np.zeros((M, K), np.float16)
+        chunk = rows[r0:r0 + M]
+        x[:chunk.shape[0]] = chunk
+        x[chunk.shape[0]:, K - 1] = 1.0
+        y = torch.full((M, K), float("nan"), dtype=torch.float32, device=DEV)
+        xs.append(x)
+        lins.append((dev(x), packed, one, y))
+    say("stack quant exhaustive", M, len(lins))
+    plan = tw.bl_stack_prepare(lins, M)
+    tw.bl_bitlinear_forward_stack(plan, len(lins), M)
+    assert tw.bl_stack_status(plan) == 0
+    for i, (x, (_, _, _, y)) in enumerate(zip(xs, lins)):
+        rq, rg, _ = oracle.quant_act_int8(x)
+        scale = (rg / np.float32(127)).astype(np.float32).astype(np.float64)
+        q = np.rint(host(y).astype(np.float64) / scale[:, None])
+        assert np.array_equal(q, rq.astype(np.float64)), (i, x[:, K - 1])
+
+
 def test_stack_read_after_write_and_write_after_read():
     """Linear 1 reads, as its fp16 x, the bytes linear 0 writes as fp32 y; linear 2 writes
     its y over linear 0's x. The stack must give the bits of three calls in order."""
@@ -661,13 +748,15 @@ def test_mf_invalid_codes():
 
 # Four-band groups x row tiles >= 160 take the staged-q kernel (N = 49152, 10240 at M = 200),
 # fewer the per-band one; 49216 leaves a last group with one band; M = 40, 70, 200 ragged
-# row tiles.
+# row tiles; M >= 256 over >= 32 band groups the 48-row tiles (300 = 6 x 48 + 12), with a
+# K split past 32768 inputs (256 x 8192 x 33792).
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 192, 320), (8, 512, 512), (16, 640, 1024),
                                    (17, 384, 448), (33, 256, 640), (64, 1024, 8192),
                                    (100, 256, 640), (2, 128, 39936), (8, 8192, 28672),
                                    (1, 49216, 64), (8, 49152, 256), (40, 49152, 192),
                                    (64, 49152, 320), (70, 49152, 128), (16, 49152, 1024),
-                                   (200, 10240, 128), (96, 2560, 256)])
+                                   (200, 10240, 128), (96, 2560, 256), (300, 8192, 1088),
+                                   (256, 8192, 33792)])
 def test_gemm_mf_acc_and_output(M, N, K):
     say("gemm mf", M, N, K)
     codes = synth.ternary_codes(synth.matrix_key(0, 131, N, K), N, K)
@@ -753,30 +842,21 @@ def _mf_q(x, wmf_eye, K):
         return y, np.rint(y.astype(np.float64) / scale[:, None])
 
 
-@pytest.mark.parametrize("M,K", [(1, 8192), (3, 2048), (8, 2048), (16, 4096)])
+@pytest.mark.parametrize("M,K", [(1, 8192), (3, 2048), (8, 2048), (16, 4096), (2, 28672)])
 def test_forward_mf_decode_quantiser_exhaustive(M, K):
-    """Every finite fp16 x against a ladder of gamma values, quantised inside the fused
+    """Every finite fp16 x against every gamma of the ladder, quantised inside the fused
     T2-MF64 decode kernel, must give the oracle's q to the bit; then degenerate rows."""
     wmf = tw.bl_pack_ternary_mf(dev(np.eye(K, dtype=np.int8)))
-    all16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
-    finite = all16[np.isfinite(all16)]
-    ladder = [np.float16(65504), np.float16(1.0), np.float16(0.0999), np.float16(6.1e-5),
-              np.float16(3.14), np.float16(127.0)]
-    if M > 2:
-        ladder = ladder[:3]
-    for gamma in ladder:
-        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(gamma)]
-        per = K - 1
-        rows = [xs[i:i + per] for i in range(0, xs.size, per)]
-        say("mf decode quant exhaustive", M, K, gamma, xs.size, len(rows))
-        for r0 in range(0, len(rows), M):
-            x = np.zeros((M, K), np.float16)
-            x[:, K - 1] = gamma
-            for m, chunk in enumerate(rows[r0:r0 + M]):
-                x[m, :chunk.size] = chunk
-            rq, _, _ = oracle.quant_act_int8(x)
-            _, q = _mf_q(x, wmf, K)
-            assert np.array_equal(q, rq.astype(np.float64)), (gamma, r0)
+    rows = ladder_rows(K)
+    say("mf decode quant exhaustive", M, K, rows.shape)
+    for r0 in range(0, rows.shape[0], M):
+        x = np.zeros((M, K), np.float16)
+        chunk = rows[r0:r0 + M]
+        x[:chunk.shape[0]] = chunk
+        x[chunk.shape[0]:, K - 1] = 1.0
+        rq, _, _ = oracle.quant_act_int8(x)
+        _, q = _mf_q(x, wmf, K)
+        assert np.array_equal(q, rq.astype(np.float64)), (r0, x[:, K - 1])
     # degenerate rows: all zero, one NaN, one inf
     x = synth.normal_fp16((M, K), 0, 95, 1)
     x[0] = 0
