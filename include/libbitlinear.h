@@ -88,7 +88,8 @@ enum bl_status {
   BL_ERR_ALIAS = 4,      /* an output buffer overlaps an input or another output */
   BL_ERR_WORKSPACE = 5,  /* ws is NULL or smaller than bl_workspace_bytes() */
   BL_ERR_HIP = 6,        /* a HIP runtime call or launch failed; see bl_last_error() */
-  BL_ERR_ARG = 7         /* any other invalid argument (e.g. an unknown path, beta_len) */
+  BL_ERR_ARG = 7,        /* any other invalid argument (e.g. an unknown path, beta_len) */
+  BL_ERR_CAPACITY = 8    /* the shape exceeds the library-owned scratch of a no-alloc call */
 };
 
 enum bl_path { BL_PATH_AUTO = 0, BL_PATH_GEMV = 1, BL_PATH_GEMM = 2 };
@@ -221,6 +222,21 @@ int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int
 int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
                          const float* beta, int64_t beta_len, int64_t N, float* y, int path,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): bl_bitlinear_forward on the GEMV path
+ * (fused quantise + add-only GEMV, same kernels, same bits) with no workspace argument. Its
+ * split-K words live in a scratch array owned by the library, one per GPU, 2 MiB, held
+ * until the process ends; the first call on a device looks up its address and queues one
+ * zero fill, and every call leaves the words zero again. The call itself allocates and
+ * frees nothing. Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give undefined outputs; order
+ * them. Arguments as bl_bitlinear_forward: x fp16 [M, K], wpacked T2-PN-64 [N, K], beta
+ * [beta_len], y fp32 [M, N]; 1 <= M <= 4, N % 64 == 0, K % 64 == 0, K <= 28672. Returns
+ * BL_ERR_CAPACITY (nothing queued) when M * N > 262144. */
+int bl_bitlinear_forward_gemv_noalloc(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
+                                      const float* beta, int64_t beta_len, int64_t N, float* y,
+                                      void* stream);
 
 /* ---- whole-stack decode in one launch ------------------------------------------------------- */
 

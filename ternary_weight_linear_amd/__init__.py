@@ -66,6 +66,7 @@ _SIGS = {
     "bl_stack_prepare": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
     "bl_bitlinear_forward_stack": (ctypes.c_int, [_P, _I64, _I64, _P, _SZ, _P]),
     "bl_stack_status": (ctypes.c_int, [_P, _P]),
+    "bl_bitlinear_forward_gemv_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P]),
 }
 
 
@@ -440,6 +441,22 @@ def bl_bitlinear_forward_mf(x, wmf, beta, N: int, out=None):
                                         N, _ptr(y), _ptr(ws), wsb, _stream(d)),
            "bl_bitlinear_forward_mf")
     return y
+
+
+def bl_bitlinear_forward_gemv_noalloc(x, wpacked, beta, out):
+    """fp16 x [M, K] -> out fp32 [M, N] (caller-allocated): the GEMV path of
+    bl_bitlinear_forward with the library's own scratch instead of a workspace; nothing is
+    allocated by this call. 1 <= M <= 4, M * N <= 262144."""
+    _half_bits(x, "x")
+    _need(wpacked, torch.uint8, "wpacked")
+    _need(out, torch.float32, "out")
+    d = _dev(x, wpacked, beta, out)
+    M, K = x.shape
+    N = out.shape[1]
+    _check(_lib.bl_bitlinear_forward_gemv_noalloc(_ptr(x), M, K, _ptr(wpacked), _ptr(beta),
+                                                  _beta_len(beta, N), N, _ptr(out), _stream(d)),
+           "bl_bitlinear_forward_gemv_noalloc")
+    return out
 
 
 def bl_stack_plan_bytes(count: int) -> int:

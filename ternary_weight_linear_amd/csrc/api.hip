@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "bl_internal.h"
 
@@ -88,6 +89,38 @@ int check_beta(const float* beta, int64_t beta_len, int64_t N) {
   return BL_OK;
 }
 
+// ---- library-owned scratch for callers that cannot allocate --------------------------
+// The split-K words of the fused decode GEMV (one uint64 per output, zero between calls)
+// for bl_bitlinear_forward_gemv_noalloc. Each GPU holds its own copy of the array; host code
+// must use the device address that hipGetSymbolAddress returns, never the array's name.
+constexpr int64_t kScratchWords = int64_t(1) << 18;   // M * N <= 262144 outputs, 2 MiB
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of the current device's scratch. The first call on a device looks the
+// address up and queues one zero fill on `s` (every call leaves the words zero again).
+int scratch_words(hipStream_t s, uint64_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward_gemv_noalloc (hipGetDevice)");
+  if (dev < 0 || dev >= kScratchDevices) return BL_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "bl_bitlinear_forward_gemv_noalloc (hipGetSymbolAddress)");
+    e = launch_fill_zero(p, sizeof(uint64_t) * kScratchWords, s);
+    if (e != hipSuccess) return hip_fail(e, "bl_bitlinear_forward_gemv_noalloc (clear)");
+    g_scratch_ptr[dev] = static_cast<uint64_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +135,8 @@ const char* bl_status_string(int status) {
     case BL_ERR_WORKSPACE: return "workspace missing or smaller than bl_workspace_bytes()";
     case BL_ERR_HIP: return "a HIP call failed (see bl_last_error)";
     case BL_ERR_ARG: return "invalid argument";
+    case BL_ERR_CAPACITY:
+      return "the shape exceeds the fixed capacity of the library's own scratch (M * N <= 262144)";
     default: return "unknown status";
   }
 }
@@ -416,6 +451,28 @@ int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wp
     e = launch_gemm(qbuf, gbuf, M, K, wpacked, beta, beta_len, N, y, nullptr, wsacc, s);
   }
   return check_launch(e, "bl_bitlinear_forward");
+}
+
+int bl_bitlinear_forward_gemv_noalloc(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
+                                      const float* beta, int64_t beta_len, int64_t N, float* y,
+                                      void* stream) {
+  if (!x || !y || !wpacked) return BL_ERR_NULL;
+  if (!dims_ok(M, N, K) || N % 64 || K % 64 || K > 28672 || M > 4) return BL_ERR_SHAPE;
+  if (M * N > kScratchWords) return BL_ERR_CAPACITY;
+  int st = check_beta(beta, beta_len, N);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(wpacked)) return BL_ERR_ALIGN;
+  const size_t yb = static_cast<size_t>(M) * N * 4;
+  if (overlap(y, yb, x, M * K * 2) || overlap(y, yb, wpacked, N * K / 4) ||
+      overlap(y, yb, beta, beta_len * 4))
+    return BL_ERR_ALIAS;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t* words = nullptr;
+  st = scratch_words(s, &words);
+  if (st) return st;
+  return check_launch(launch_gemv_fused(x, static_cast<int>(M), K, wpacked, beta, beta_len, N, y,
+                                        words, nullptr, s),
+                      "bl_bitlinear_forward_gemv_noalloc");
 }
 
 size_t bl_stack_plan_bytes(int64_t count) {

@@ -11,7 +11,7 @@ import pytest
 LIB_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                         "ternary_weight_linear_amd", "libbitlinear.so")
 
-OK, NULL, SHAPE, ALIGN, ALIAS, WS, HIP, ARG = range(8)
+OK, NULL, SHAPE, ALIGN, ALIAS, WS, HIP, ARG, CAPACITY = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -29,8 +29,8 @@ def test_exports_every_header_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    for s in range(8):
-        assert lib.bl_status_string(s)
+    for s in range(9):
+        assert lib.bl_status_string(s) and lib.bl_status_string(s) != b"unknown status"
     assert lib.bl_status_string(99) == b"unknown status"
     assert lib.bl_version() >= 10000
     assert lib.bl_last_error() == b""
@@ -242,3 +242,21 @@ def test_mf_checks(lib):
     assert fwd(x=_p(A + 2)) == ALIGN
     assert fwd(wsb=100) == WS
     assert fwd(y=_p(A + 16)) == ALIAS
+
+
+def test_noalloc_gemv_checks(lib):
+    """The no-alloc decode entry point rejects bad arguments, and shapes beyond its scratch
+    (M * N > 262144), before touching the GPU."""
+    f = lib.bl_bitlinear_forward_gemv_noalloc
+    K, N = 256, 1024
+    assert f(None, 1, K, _p(B), _p(C), 1, N, _p(D), None) == NULL
+    assert f(_p(A), 5, K, _p(B), _p(C), 1, N, _p(D), None) == SHAPE          # M > 4
+    assert f(_p(A), 1, 100, _p(B), _p(C), 1, N, _p(D), None) == SHAPE        # K % 64
+    assert f(_p(A), 1, 28736, _p(B), _p(C), 1, N, _p(D), None) == SHAPE      # K > 28672
+    assert f(_p(A), 4, K, _p(B), _p(C), 1, 65600, _p(D), None) == CAPACITY   # M * N > 2^18
+    assert f(_p(A), 1, K, _p(B), _p(C), 1, 262208, _p(D), None) == CAPACITY
+    assert f(_p(A), 1, K, _p(B), None, 1, N, _p(D), None) == NULL
+    assert f(_p(A), 1, K, _p(B), _p(C), 7, N, _p(D), None) == ARG            # beta_len
+    assert f(_p(A + 2), 1, K, _p(B), _p(C), 1, N, _p(D), None) == ALIGN
+    assert f(_p(A), 1, K, _p(B), _p(C), 1, N, _p(A + 64), None) == ALIAS     # y over x
+    assert f(_p(A), 1, K, _p(B), _p(C), 1, N, _p(B + 128), None) == ALIAS    # y over weights
