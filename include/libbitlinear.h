@@ -129,8 +129,10 @@ int bl_ternarize_absmean(const float* W, int64_t N, int64_t K, int8_t* codes, vo
  * int32, may be NULL). N % 64 == 0, K % 64 == 0; codes and packed 16-byte aligned. */
 int bl_pack_ternary(const int8_t* codes, int64_t N, int64_t K, void* packed,
                     int32_t* n_invalid, void* stream);
-/* Inverse of bl_pack_ternary. A (P, N) = (1, 1) pair decodes to 0 and adds 1 to
- * *n_invalid (may be NULL). */
+/* Inverse of bl_pack_ternary ([b158] "BitNet b1.58 介绍": every weight is -1, 0 or +1):
+ * int8 codes [N, K] in {-1, 0, +1}. A (P, N) = (1, 1) pair decodes to 0 and adds 1 to
+ * *n_invalid (may be NULL). Shapes and alignment as bl_pack_ternary; codes must not
+ * overlap packed. */
 int bl_unpack_ternary(const void* packed, int64_t N, int64_t K, int8_t* codes,
                       int32_t* n_invalid, void* stream);
 
@@ -148,7 +150,8 @@ int bl_repack_ternary_mf(const void* t2pn, int64_t N, int64_t K, void* mf, int32
  * 能力": Sign(W) is what inference keeps). Bit set iff W < 0, so +0, -0 and NaN give +1.
  * N % 64 == 0, K % 128 == 0; W and packed 16-byte aligned. */
 int bl_pack_sign(const float* W, int64_t N, int64_t K, void* packed, void* stream);
-/* Inverse of bl_pack_sign: int8 signs [N, K] in {-1, +1}. */
+/* Inverse of bl_pack_sign ([onebit] "1. 新的1bit结构": the weight matrix holds only +-1):
+ * int8 signs [N, K] in {-1, +1}. N % 64 == 0, K % 128 == 0; signs must not overlap packed. */
 int bl_unpack_sign(const void* packed, int64_t N, int64_t K, int8_t* signs, void* stream);
 
 /* ---- b1.58 forward ------------------------------------------------------------------------- */
@@ -177,7 +180,9 @@ int bl_bitlinear_gemv(const uint32_t* planes, const float* gamma, int64_t M, int
 
 /* Batched / prefill GEMM with int8 matrix cores ([b158] "实验及结果": batched throughput at
  * sequence length 512). Same result as bl_bitlinear_gemv for any M >= 1: the packed
- * weights are expanded to int8 tiles in LDS and multiplied by q with int32 accumulation.
+ * weights are expanded to int8 operands and multiplied by q with int32 accumulation
+ * (M <= 64: expanded in registers as they stream in; M > 64: expanded once per output
+ * tile into LDS and shared by the workgroup's waves).
  * q int8 [M, K] (16-byte aligned rows), other arguments as bl_bitlinear_gemv. Uses ws. */
 int bl_bitlinear_gemm(const int8_t* q, const float* gamma, int64_t M, int64_t K,
                       const void* wpacked, const float* beta, int64_t beta_len, int64_t N,
@@ -208,15 +213,17 @@ int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void*
                             size_t ws_bytes, void* stream);
 
 /* Debug: the int32 accumulators acc[m,n] = sum_k w[n,k] q[m,k] of the chosen kernel path,
- * before the epilogue. path BL_PATH_GEMV needs planes (M <= 4), BL_PATH_GEMM needs q,
+ * before the epilogue ([b158] "实验及结果", Fig. 3: the product of ternary weights and int8
+ * activations is a sum of int8 terms, so it has exactly one correct int32 value). path BL_PATH_GEMV needs planes (M <= 4), BL_PATH_GEMM needs q,
  * BL_PATH_AUTO takes the path bl_bitlinear_forward would take (and needs its operand).
  * acc int32 [M, N]. Uses ws. */
 int bl_bitlinear_acc_i32(const int8_t* q, const uint32_t* planes, int64_t M, int64_t K,
                          const void* wpacked, int64_t N, int32_t* acc, int path, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* The whole b1.58 linear from fp16 activations: quantise, then GEMV (M <= 2) or GEMM, then
- * rescale. x fp16 [M, K]; other arguments as bl_bitlinear_gemm. path selects the kernel
+/* The whole b1.58 linear from fp16 activations ([b158] "BitNet b1.58 介绍": BitLinear takes
+ * the place of nn.Linear, with per-token absmax activations and no bias): quantise, then
+ * GEMV (M <= 2) or GEMM, then rescale. x fp16 [M, K]; other arguments as bl_bitlinear_gemm. path selects the kernel
  * (BL_PATH_AUTO picks by M). Uses ws (bl_workspace_bytes(M, N, K)), which also holds the
  * quantised activations. */
 int bl_bitlinear_forward(const uint16_t* x, int64_t M, int64_t K, const void* wpacked,
