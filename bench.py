@@ -35,7 +35,10 @@ METRIC = "BitLinear GEMV effective HBM GB/s (% peak); int8 TOPS at M=512 (% peak
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode70b_m1_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", "gemv.hip")
+# the dominant kernel's sources: its file and the device helpers it includes
+KERNEL_SOURCES = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
+                  for f in ("gemv.hip", "bl_internal.h")]
+CEIL_LIB = os.path.join(ROOT, "ternary_weight_linear_amd", "libblceil.so")
 
 
 def log(*a):
@@ -53,6 +56,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="launch the pass eagerly (profilers)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run a plain 1 GiB device copy (HBM counter calibration) and exit")
+    p.add_argument("--ceilings", action="store_true",
+                   help="measure the streaming-read and int8 matrix-core ceilings only")
     return p.parse_args()
 
 
@@ -441,18 +446,57 @@ def bench_residual(torch, tw, synth, dev, steps, warmup, pool=128):
 
 
 # ------------------------------------------------------------------------------------------
+# measured ceilings (ternary_weight_linear_amd/csrc/ceilings.hip)
+# ------------------------------------------------------------------------------------------
+def measured_ceilings(torch, dev):
+    """Streaming HBM read of a 4 GiB buffer (16 x the 256 MB MALL) and an int8 matrix-core
+    loop, both timed with HIP events on the launch stream; best of a few launch shapes."""
+    import ctypes
+    lib = ctypes.CDLL(CEIL_LIB)
+    lib.bl_ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.bl_ceil_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bl_ceil_mfma_i8_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.bl_ceil_mfma_i8_ops.restype = ctypes.c_double
+    P = ctypes.c_void_p
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    best_read = 0.0
+    read_grid = None
+    for grid in (1024, 2048, 4096, 8192):
+        out = torch.zeros(grid, dtype=torch.int32, device=dev)
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        ms = timed(torch, lambda: lib.bl_ceil_stream_read(P(buf.data_ptr()), nbytes, P(out.data_ptr()),
+                                                          grid, stream), 5, 2)
+        gbs = nbytes / (ms / 1e3) / 1e9
+        if gbs > best_read:
+            best_read, read_grid = gbs, grid
+    del buf
+    best_mfma = 0.0
+    mfma_grid = None
+    iters = 4000
+    for grid in (512, 1024, 2048):
+        out = torch.empty(grid * 256 * 4, dtype=torch.int32, device=dev)
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        ms = timed(torch, lambda: lib.bl_ceil_mfma_i8(iters, grid, P(out.data_ptr()), stream), 5, 2)
+        tops = lib.bl_ceil_mfma_i8_ops(iters, grid) / (ms / 1e3) / 1e12
+        if tops > best_mfma:
+            best_mfma, mfma_grid = tops, grid
+    return {"hbm_read_gbs": round(best_read, 1), "hbm_read_frac_spec": round(best_read / HBM_PEAK_GBS, 4),
+            "hbm_read_kernel": f"stream_read_kernel, 4 GiB read once, {read_grid} workgroups",
+            "int8_mfma_tops": round(best_mfma, 1), "int8_mfma_frac_spec": round(best_mfma / INT8_PEAK_TOPS, 4),
+            "int8_mfma_kernel": f"mfma_i8_kernel (v_mfma_i32_16x16x64_i8, 8 independent accumulators "
+                                f"per wave), {mfma_grid} workgroups of 4 waves"}
+
+
+# ------------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ------------------------------------------------------------------------------------------
-def cpu_baseline(synth, budget_s=12.0):
-    import threadpoolctl
+def _oracle_leg(synth, mats, budget_s):
+    """Time the oracle's quantise + exact accumulate + rescale over (codes, x) pairs for about
+    budget_s seconds; returns (repetitions, seconds)."""
     import oracle
-    rows = 512
-    layer = 0
-    mats = []
-    for mid, (name, N, K) in enumerate(synth.LLAMA70B_LINEARS):
-        codes = synth.ternary_codes(synth.matrix_key(0, 5, layer, mid), N, K, rows=np.arange(rows))
-        x = synth.normal_fp16((1, K), 0, 5, 1000 + layer, mid)
-        mats.append((codes, x))
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -462,15 +506,45 @@ def cpu_baseline(synth, budget_s=12.0):
             oracle.bitlinear_output(acc, gamma, synth.BETA_DIRECT)
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    packed_bytes = reps * sum(c.size for c, _ in mats) / 4
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": packed_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"70B-shaped layer 0, first {rows} rows of each of the 7 linears, M=1; "
-                      f"oracle quantise + exact accumulate + rescale, {reps} repetitions in {dt:.1f} s; "
-                      f"GB/s counts the 2-bit packed bytes those rows would occupy",
-            "host_cpus": os.cpu_count()}
+            return reps, time.perf_counter() - t0
+
+
+def cpu_baseline(synth, budget_s=6.0):
+    """The CPU oracle as it stands, on bounded samples of three workloads: the headline leg
+    (70B layer 0, first 512 rows of each linear, M = 1) with all host threads and with one,
+    the 7B decode set (first 512 rows of each linear, M = 1) and the 3B prefill set (first
+    64 rows of each linear, M = 512 tokens)."""
+    import threadpoolctl
+    def sample(linears, key_cfg, rows, M, x_keys):
+        mats = []
+        for mid, (name, N, K) in enumerate(linears):
+            codes = synth.ternary_codes(synth.matrix_key(0, key_cfg, 0, mid), N, K, rows=np.arange(rows))
+            mats.append((codes, synth.normal_fp16((M, K), *x_keys, mid)))
+        return mats
+    legs = {}
+    threads_all = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    m70 = sample(synth.LLAMA70B_LINEARS, 5, 512, 1, (0, 5, 1000))
+    for name, limit in (("70b_m1_all_threads", None), ("70b_m1_1_thread", 1)):
+        with threadpoolctl.threadpool_limits(limits=limit):
+            reps, dt = _oracle_leg(synth, m70, budget_s)
+        legs[name] = {"gbs_packed": reps * sum(c.size for c, _ in m70) / 4 / dt / 1e9,
+                      "threads": limit or int(threads_all), "reps": reps, "s": round(dt, 2)}
+    m7 = sample(synth.LLAMA7B_LINEARS, 3, 512, 1, (0, 3, 2000))
+    reps, dt = _oracle_leg(synth, m7, budget_s / 2)
+    legs["7b_m1_all_threads"] = {"gbs_packed": reps * sum(c.size for c, _ in m7) / 4 / dt / 1e9,
+                                 "threads": int(threads_all), "reps": reps, "s": round(dt, 2)}
+    m3 = sample(synth.LLAMA3B_LINEARS, 4, 64, 512, (0, 4, 3000))
+    reps, dt = _oracle_leg(synth, m3, budget_s / 2)
+    legs["3b_m512_all_threads"] = {"tops": reps * sum(2 * 512 * c.size for c, _ in m3) / dt / 1e12,
+                                   "threads": int(threads_all), "reps": reps, "s": round(dt, 2)}
+    main = legs["70b_m1_all_threads"]
+    return {"value": main["gbs_packed"], "unit": "GB/s", "cores": main["threads"], "kind": "oracle",
+            "sample": "70B-shaped layer 0, first 512 rows of each of the 7 linears, M=1; oracle "
+                      "quantise + exact accumulate + rescale, repeated for ~6 s; GB/s counts the 2-bit "
+                      "packed bytes those rows would occupy. Legs: the same with one thread; 7B decode "
+                      "set (512 rows per linear, M=1); 3B prefill set (64 rows per linear, M=512, int8 TOPS)",
+            "legs": legs, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def bench_decode70b_stack(torch, tw, synth, dev, layers, M, steps, warmup):
@@ -506,10 +580,37 @@ def kernel_traffic():
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if t.get("source_sha256") != src:
+    if t.get("source_sha256") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_prefill3b_m512_mfma.json")
+GEMM_SOURCES = [os.path.join(ROOT, "ternary_weight_linear_amd", "csrc", f)
+                for f in ("tern_mfma.hip", "bl_internal.h")]
+
+
+def mfma_counters():
+    """Matrix-core utilisation of the prefill GEMM from the committed rocprofv3 counter
+    summary, or None if it is missing or was taken from different kernel sources."""
+    try:
+        t = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(f, "rb").read())
+    if t.get("source_sha256") != h.hexdigest():
+        return None
+    return t.get("summary")
+
+
+def kernel_source_hash():
+    """sha256 over the dominant kernel's source files, in order."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def main():
@@ -538,6 +639,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": a.numel()}))
         return
 
+    if args.ceilings:
+        print(json.dumps({"measured_ceilings": measured_ceilings(torch, dev)}))
+        return
+
     if args.only in ("prefill3b", "decode7b", "decode7b_stack", "onebit", "residual"):
         fn = {"prefill3b": lambda: bench_prefill3b(torch, tw, synth, dev, args.steps, args.warmup),
               "decode7b": lambda: bench_decode7b(torch, tw, sgpu, synth, dev, args.steps, args.warmup),
@@ -547,6 +652,10 @@ def main():
         print(json.dumps({args.only: fn()}))
         return
 
+    ceilings = None
+    if not args.skip_extra:
+        ceilings = measured_ceilings(torch, dev)
+        log("measured ceilings:", json.dumps(ceilings))
     t0 = time.time()
     log("building the 70B-shaped packed stack (17.1 GB) ...")
     layers = build_stack70b(torch, tw, sgpu, synth, dev)
@@ -611,10 +720,25 @@ def main():
 
     ms = main_res["ms_per_pass"]
     launches = main_res["launches_per_pass"]
-    per_launch_bytes = main_res["weight_bytes"] / launches
+    # algorithmic bytes per launch: packed weights + fp16 x + fp32 y, averaged over the pass;
+    # the launch duration is the pass time (HIP events on the launch stream) per launch, so
+    # it includes the gap between consecutive graph launches
+    per_launch_bytes = main_res["algo_bytes"] / launches
     avg_launch_s = ms / 1e3 / launches
     achieved = per_launch_bytes / avg_launch_s / 1e9
     traffic = kernel_traffic()
+    roofline_gemm = None
+    if "prefill3b_m512" in extra:
+        pf = extra["prefill3b_m512"]
+        roofline_gemm = {"bound": "mfma", "kernel": "tern_mfq_kernel<FM> (staged-q int8 MFMA, T2-MF64)",
+                         "workload": "3B-shaped prefill, M=512: q|k|v 512x9600x3200, o 512x3200x3200, "
+                                     "gate|up 512x17280x3200, down 512x3200x8640",
+                         "achieved": round(pf["tops_gemms"], 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(pf["tops_gemms"] / INT8_PEAK_TOPS, 4),
+                         "int8_ops_per_pass": pf["int8_ops"], "ms_gemms": round(pf["ms_gemms_only"], 4),
+                         "mfma_counters": mfma_counters()}
+        if ceilings:
+            roofline_gemm["frac_measured_peak"] = round(pf["tops_gemms"] / ceilings["int8_mfma_tops"], 4)
     out = {
         "metric": METRIC,
         "value": round(main_res["gbs"], 2),
@@ -641,7 +765,11 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
-                     "algorithmic_bytes_per_launch": round(per_launch_bytes, 1)},
+                     "algorithmic_bytes_per_launch": round(per_launch_bytes, 1),
+                     "frac_measured_peak": (round(achieved / ceilings["hbm_read_gbs"], 4)
+                                            if ceilings else None)},
+        "roofline_gemm": roofline_gemm,
+        "measured_ceilings": ceilings,
         "extra": extra,
     }
     if not args.skip_cpu:

@@ -1,4 +1,5 @@
-"""Compile libbitlinear (and the synthetic-input helper library) for gfx950 with hipcc.
+"""Compile libbitlinear (and the synthetic-input and measured-ceiling helper libraries) for
+gfx950 with hipcc.
 
     python ternary_weight_linear_amd/build.py        # builds both .so files in-tree
 
@@ -20,6 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libbitlinear.so")
 SYNTH_DIR = os.path.join(ROOT, "synth")
 SYNTH_LIB_PATH = os.path.join(SYNTH_DIR, "libblsynth.so")
+# measured ceilings (streaming read, int8 matrix-core loop) for the benchmark's rooflines
+CEIL_LIB_PATH = os.path.join(PKG, "libblceil.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = os.environ.get("BL_OFFLOAD_ARCH", "gfx950")
@@ -66,16 +69,23 @@ def build(verbose: bool = False) -> str:
                                   ["-fvisibility=hidden", *EXTRA.get(s, [])]))
         jsyn = ex.submit(_compile, os.path.join(SYNTH_DIR, "csrc", "synth.hip"),
                          os.path.join(BUILD_DIR, "synth.o"), [])
+        jceil = ex.submit(_compile, os.path.join(CSRC, "ceilings.hip"),
+                          os.path.join(BUILD_DIR, "ceilings.o"), [],
+                          ["-fvisibility=hidden", "-mllvm", "-amdgpu-mfma-vgpr-form"])
         objs = [j.result() for j in jobs]
         syn_obj = jsyn.result()
+        ceil_obj = jceil.result()
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
     tmp = SYNTH_LIB_PATH + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", syn_obj, "-o", tmp])
     os.replace(tmp, SYNTH_LIB_PATH)
+    tmp = CEIL_LIB_PATH + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", ceil_obj, "-o", tmp])
+    os.replace(tmp, CEIL_LIB_PATH)
     if verbose:
-        print("built", LIB_PATH, "and", SYNTH_LIB_PATH)
+        print("built", LIB_PATH, SYNTH_LIB_PATH, "and", CEIL_LIB_PATH)
     return LIB_PATH
 
 
