@@ -406,6 +406,29 @@ def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
         out[f"M{M}"] = dict(us_per_layer=ms * 1e3 / pool, us_per_layer_eager=ms_eager * 1e3 / pool,
                             gbs_signs=pool * N * K / 8 / (ms / 1e3) / 1e9,
                             stored_bits_per_layer=8 * spool[0].numel() + 16 * (N + K), graph=True)
+    # a 70B-sized matrix (28672 x 8192, 29 MiB of signs) at M = 1, pool of 16
+    N2, K2, pool2 = 28672, 8192, 16
+    W = torch.from_numpy(synth.normal_fp32((N2, K2), 0, 2, 5, 0)).to(dev)
+    base = tw.bl_pack_sign(W)
+    del W
+    spool2 = [base] + [torch.roll(base, shifts=s) for s in range(1, pool2)]
+    g2 = torch.from_numpy(synth.uniform_fp16((K2,), 0.5, 1.5, 0, 2, 6)).to(dev)
+    h2 = torch.from_numpy(synth.uniform_fp16((N2,), 0.5, 1.5, 0, 2, 7)).to(dev)
+    x2 = torch.from_numpy(synth.normal_fp16((1, K2), 0, 2, 8)).to(dev)
+    y2 = torch.empty((1, N2), dtype=torch.float32, device=dev)
+    ws2 = tw.workspace(dev, tw.bl_workspace_bytes(1, N2, K2))
+
+    def sweep2():
+        stream = P(torch.cuda.current_stream().cuda_stream)
+        for sp in spool2:
+            assert lib.bl_onebit_linear(P(x2.data_ptr()), P(g2.data_ptr()), P(sp.data_ptr()),
+                                        P(h2.data_ptr()), 1, N2, K2, P(y2.data_ptr()),
+                                        P(ws2.data_ptr()), ws2.numel(), stream) == 0
+
+    run, keep = graphed(torch, sweep2)
+    ms = timed(torch, run, max(2, steps // 4), 1)
+    out["28672x8192_M1"] = dict(us_per_layer=ms * 1e3 / pool2,
+                                gbs_signs=pool2 * N2 * K2 / 8 / (ms / 1e3) / 1e9, graph=True)
     return out
 
 

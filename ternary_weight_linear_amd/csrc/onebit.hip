@@ -14,7 +14,7 @@ namespace bl {
 
 size_t onebit_part_floats(int64_t M, int64_t N, int64_t K) {
   if (N % 64 || K % 128) return 0;
-  return sign_mfma_part_floats(M, N, K);
+  return sign_mfma_part_floats(M, N, K, false);
 }
 
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,

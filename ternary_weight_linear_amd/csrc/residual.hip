@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void residual_pack_kernel(
 
 size_t residual_part_floats(int64_t M, int64_t N, int64_t K) {
   if (N % 64 || K % 128) return 0;
-  return sign_mfma_part_floats(M, N, K);
+  return sign_mfma_part_floats(M, N, K, true);
 }
 
 hipError_t launch_residual_binarize(const float* W, int64_t N, int64_t K, void* planes_o,

@@ -267,41 +267,287 @@ __global__ __launch_bounds__(256) void sign_mfma_kernel(const SignMfmaArgs a) {
   if (tid == 0) reset_agent(&a.cnt[cidx]);
 }
 
-struct SignPlan { int64_t bands, mtiles, nsplit, tps; };
+// ---- staged kernel: decode-sized batches (M <= 4) --------------------------------------
+// A workgroup of kStWaves waves owns NF 16-column fragments of a band (NF = 4: the whole
+// band; NF = 1: fragment f0, so that a layer of few bands still fills the chip without
+// splitting K) and a range of 128-input tiles. It stages x (M rows) and g of its range in
+// LDS with all threads at once and issues every sign word its waves need in the same burst
+// (the lane's S1-128 record, or only word f0 of it), so a wave waits for memory about once
+// instead of once per tile or two; then it multiplies: A = x from LDS (lanes of rows past M
+// read row M - 1; those output rows are never stored), B = g from LDS with the sign bits
+// assigned, one v_mfma_f32_16x16x32_f16 per fragment and 32-input slice. The waves' sums
+// meet in LDS (over the staging buffer) in wave order.
+constexpr int kStWaves = 8;
+constexpr int kStLdsBytes = 48 * 1024;                 // x rows and g of one range
+constexpr int kStStage = kStLdsBytes / 16 / (64 * kStWaves);   // 16-byte pieces per thread
+// 128-input tiles one range may hold: M rows of x and (OneBit) g, 256 bytes each per tile.
+__host__ __device__ constexpr int st_max_tiles(int64_t M) {
+  return static_cast<int>(kStLdsBytes / ((M + 1) * 256));
+}
+constexpr int kStMaxPerWave = (st_max_tiles(1) + kStWaves - 1) / kStWaves;
+// PW: tiles per wave the kernel is built for (4 or kStMaxPerWave): every one of them is
+// loaded (clamped into the range), so short ranges take the small build.
+template <bool RES, int NF, int PW>
+__global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMfmaArgs a) {
+  constexpr int kPad = 68;
+  static_assert(kStWaves * 4 * NF * kPad * 4 <= kStLdsBytes, "reduction fits the staging buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t st[kStLdsBytes / 2];
+  __shared__ uint32_t s_arrived;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int64_t band = NF == 4 ? blockIdx.x : blockIdx.x >> 2;
+  const int f0 = NF == 4 ? 0 : static_cast<int>(blockIdx.x & 3);
+  const int split = blockIdx.z, nsplit = gridDim.z;
+  const int M = static_cast<int>(a.M);
+  const int KT = static_cast<int>(a.K / 128);
+  const int t0 = split * a.tiles_per_split;
+  const int t1 = min(KT, t0 + a.tiles_per_split);
+  const int nt = max(t1 - t0, 0);
+
+  // 1. issue the staging loads (x rows, then g), then every sign word of this wave's tiles.
+  // Every load is unconditional (indices past the range are clamped into it): loads under
+  // branches made the compiler wait for each one before issuing the next.
+  const int xpieces = M * nt * 16, npieces = xpieces + (RES ? 0 : nt * 16);
+  sm_u32x4 sv[kStStage];
+#pragma unroll
+  for (int i = 0; i < kStStage; ++i) {
+    const int pc = min(tid + 64 * kStWaves * i, npieces - 1);
+    const int m = pc / (nt * 16), q = pc - m * nt * 16;   // m == M: g
+    const uint16_t* src = m < M ? a.x + static_cast<int64_t>(m) * a.K : a.g;
+    sv[i] = *reinterpret_cast<const sm_u32x4*>(src + static_cast<int64_t>(t0) * 128 + 8 * q);
+  }
+  const int first = t0 + wave;
+  const int n = first < t1 ? (t1 - first + kStWaves - 1) / kStWaves : 0;
+  uint32_t w0[PW][NF], w1[RES ? PW : 1][NF];
+  float c0[RES ? PW : 1][NF], c1[RES ? PW : 1][NF];
+  const uint32_t soff = 16u * lane + 4u * static_cast<uint32_t>(f0);
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    {
+      const int t = min(first + kStWaves * j, t1 - 1);
+      const char* rec0 = reinterpret_cast<const char*>(a.p0) + ((band * KT + t) << 10);
+      const char* rec1 = reinterpret_cast<const char*>(a.p1) + ((band * KT + t) << 10);
+      if constexpr (NF == 4) {
+        const sm_u32x4 r0 = sm_load<sm_u32x4>(rec0, soff);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) w0[j][f] = r0[f];
+        if constexpr (RES) {
+          const sm_u32x4 r1 = sm_load<sm_u32x4>(rec1, soff);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) w1[j][f] = r1[f];
+        }
+      } else {
+        w0[j][0] = sm_load<uint32_t>(rec0, soff);
+        if constexpr (RES) w1[j][0] = sm_load<uint32_t>(rec1, soff);
+      }
+      if constexpr (RES) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int64_t ci = (band * 64 + 16 * (NF == 4 ? f : f0) + r16) * KT + t;
+          c0[j][f] = a.a0[ci];
+          c1[j][f] = a.a1[ci];
+        }
+      }
+    }
+  }
+  // 2. staged pieces to LDS: x row m at m * nt * 128 halves, g after the M rows
+#pragma unroll
+  for (int i = 0; i < kStStage; ++i) {
+    const int pc = tid + 64 * kStWaves * i;
+    if (pc < npieces) *reinterpret_cast<sm_u32x4*>(st + 8 * pc) = sv[i];
+  }
+  __syncthreads();
+
+  // 3. products: lane (grp, r16) feeds row min(r16, M - 1) of x and column 16 f + r16
+  const uint16_t* xrow = st + static_cast<int64_t>(min(r16, M - 1)) * nt * 128 + 8 * grp;
+  const uint16_t* grow = st + static_cast<int64_t>(M) * nt * 128 + 8 * grp;
+  sm_f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = sm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    if (j < n) {
+      const int tl = wave + kStWaves * j;   // tile within the range
+      sm_f32x4 pp[NF], rr[NF];
+      if constexpr (RES) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) pp[f] = rr[f] = sm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      auto slice = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        const sm_f16x8 av = *reinterpret_cast<const sm_f16x8*>(xrow + tl * 128 + 32 * S);
+        if constexpr (!RES) {
+          const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            sm_u32x4 b;
+            b[0] = gv[0] ^ sign_pair_bits<S, 0>(w0[j][f]);
+            b[1] = gv[1] ^ sign_pair_bits<S, 1>(w0[j][f]);
+            b[2] = gv[2] ^ sign_pair_bits<S, 2>(w0[j][f]);
+            b[3] = gv[3] ^ sign_pair_bits<S, 3>(w0[j][f]);
+            acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b), acc[f], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            sm_u32x4 b0, b1;
+            b0[0] = a.one ^ sign_pair_bits<S, 0>(w0[j][f]);
+            b0[1] = a.one ^ sign_pair_bits<S, 1>(w0[j][f]);
+            b0[2] = a.one ^ sign_pair_bits<S, 2>(w0[j][f]);
+            b0[3] = a.one ^ sign_pair_bits<S, 3>(w0[j][f]);
+            b1[0] = a.one ^ sign_pair_bits<S, 0>(w1[j][f]);
+            b1[1] = a.one ^ sign_pair_bits<S, 1>(w1[j][f]);
+            b1[2] = a.one ^ sign_pair_bits<S, 2>(w1[j][f]);
+            b1[3] = a.one ^ sign_pair_bits<S, 3>(w1[j][f]);
+            pp[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b0), pp[f], 0, 0, 0);
+            rr[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b1), rr[f], 0, 0, 0);
+          }
+        }
+      };
+      slice(std::integral_constant<int, 0>{});
+      slice(std::integral_constant<int, 1>{});
+      slice(std::integral_constant<int, 2>{});
+      slice(std::integral_constant<int, 3>{});
+      if constexpr (RES) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f][i] += c0[j][f] * pp[f][i] + c1[j][f] * rr[f][i];
+      }
+    }
+  }
+
+  // D layout: lane l holds rows 4*(l/16) + i of x, column l % 16 of fragment f. The sums
+  // meet in the staging buffer once every wave is done reading it.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(st);
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 4 * NF + 4 * f + i) * kPad + lane] = acc[f][i];
+  __syncthreads();
+  // output o = tid + 512 j: row ml = o / (16 NF) of x, column nl = o % (16 NF) of the
+  // workgroup's columns (threads past the 256 NF outputs only take part in the barriers)
+  constexpr int kOutPer = NF == 4 ? 2 : 1;
+  float sum[kOutPer];
+  int64_t ncol[kOutPer];
+  int ml[kOutPer];
+  bool live[kOutPer];
+#pragma unroll
+  for (int q = 0; q < kOutPer; ++q) {
+    const int o = tid + 64 * kStWaves * q;
+    ml[q] = (o / (16 * NF)) & 15;
+    const int nl = o % (16 * NF);
+    const int idx = (4 * (nl >> 4) + (ml[q] & 3)) * kPad + 16 * (ml[q] >> 2) + (nl & 15);
+    float acc_s = red[idx];
+#pragma unroll
+    for (int w = 1; w < kStWaves; ++w) acc_s += red[w * 4 * NF * kPad + idx];
+    sum[q] = acc_s;
+    ncol[q] = band * 64 + 16 * f0 + nl;
+    live[q] = o < 256 * NF && ml[q] < M;
+  }
+  float hn[kOutPer];
+#pragma unroll
+  for (int q = 0; q < kOutPer; ++q) hn[q] = RES ? 1.0f : half_bits_to_float(a.h[ncol[q]]);
+  if (nsplit == 1) {
+#pragma unroll
+    for (int q = 0; q < kOutPer; ++q)
+      if (live[q]) a.y[static_cast<int64_t>(ml[q]) * a.N + ncol[q]] = RES ? sum[q] : sum[q] * hn[q];
+    return;
+  }
+  // nsplit > 1 only when M * N < 2^30 (see plan_sign_mfma): element offsets fit 32 bits.
+  const int64_t MN = a.M * a.N;
+  uint32_t po[kOutPer];
+#pragma unroll
+  for (int q = 0; q < kOutPer; ++q) {
+    po[q] = static_cast<uint32_t>(ml[q] * a.N + ncol[q]);
+    if (live[q]) atomic_store_agent(a.part + split * MN + po[q], sum[q]);
+  }
+  wait_own_memory_ops();
+  __syncthreads();
+  if (tid == 0) s_arrived = arrive_agent(&a.cnt[blockIdx.x]);
+  __syncthreads();
+  if (s_arrived != static_cast<uint32_t>(nsplit - 1)) return;   // uniform over the workgroup
+#pragma unroll
+  for (int q = 0; q < kOutPer; ++q) {
+    float v[kSignMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kSignMaxSplits; ++sp)
+      v[sp] = (sp < nsplit && live[q]) ? atomic_load_agent(a.part + sp * MN + po[q]) : 0.0f;
+    float t = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kSignMaxSplits; ++sp)
+      if (sp < nsplit) t += v[sp];                      // split order
+    if (live[q]) a.y[static_cast<int64_t>(ml[q]) * a.N + ncol[q]] = RES ? t : t * hn[q];
+  }
+  if (tid == 0) reset_agent(&a.cnt[blockIdx.x]);
+}
+
+// kernel: 0 = band kernel (sign_mfma_kernel), 1 = staged kernel with one fragment per
+// workgroup, 4 = staged kernel with one band per workgroup.
+struct SignPlan { int64_t cols, mtiles, nsplit, tps; int kernel; };
 
 // Workgroups to aim for. Tuning harnesses that compile the sources directly may set it
 // (0 = the default); the workspace is sized for the default.
 constexpr int64_t kSignWgTarget = 256;
 inline int64_t sign_wg_target() { return kSignWgTarget; }
 
-// Splits K across workgroups only while bands x x-tiles leaves the chip short of `target`
-// workgroups; each split keeps at least one tile per wave.
-inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target) {
+// Decode-sized batches (M <= 4) take the staged kernel: one fragment per workgroup where
+// the bands alone leave the chip short of `target` workgroups, one band per workgroup
+// otherwise (OneBit only: the residual's two planes and scales would not fit the registers of
+// a deep burst). K is split across workgroups while the workgroups still fall short of
+// `target`, and for the staged kernel also where a range would not fit its LDS (at most
+// kSignMaxSplits splits; beyond that the band kernel); each split keeps at least one tile
+// per wave.
+inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, bool res) {
   const int64_t KT = K / 128, bands = N / 64, mtiles = (M + 15) / 16;
-  int64_t nsplit = (target + bands * mtiles - 1) / (bands * mtiles);
-  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / 4));
+  const int64_t need = (KT + st_max_tiles(M) - 1) / st_max_tiles(M);   // splits the LDS needs
+  int kernel = 0;
+  if (M <= 4 && need <= kSignMaxSplits) kernel = bands < target ? 1 : (res ? 0 : 4);
+  // a K split needs one counter per workgroup column and 32-bit element offsets
+  auto can_split = [&](int k) {
+    return mtiles * (k == 1 ? 4 * bands : bands) <= kMaxCounters && M * N < (int64_t(1) << 30);
+  };
+  if (kernel != 0 && need > 1 && !can_split(kernel)) kernel = 0;
+  const int64_t cols = kernel == 1 ? 4 * bands : bands;
+  const int64_t per_wave = kernel ? kStWaves : 4;
+  int64_t nsplit = (target + cols * mtiles - 1) / (cols * mtiles);
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / per_wave));
+  if (kernel) nsplit = std::max<int64_t>(nsplit, need);
   nsplit = std::min<int64_t>(std::max<int64_t>(nsplit, 1), kSignMaxSplits);
-  if (mtiles * bands > kMaxCounters || M * N >= (int64_t(1) << 30)) nsplit = 1;
+  if (!can_split(kernel)) nsplit = 1;
   const int64_t tps = (KT + nsplit - 1) / nsplit;
-  return {bands, mtiles, (KT + tps - 1) / tps, tps};
+  return {cols, mtiles, (KT + tps - 1) / tps, tps, kernel};
 }
 
 template <bool RES>
 inline hipError_t launch_sign_mfma(const SignMfmaArgs& args, hipStream_t s) {
-  const SignPlan p = plan_sign_mfma(args.M, args.N, args.K, sign_wg_target());
+  const SignPlan p = plan_sign_mfma(args.M, args.N, args.K, sign_wg_target(), RES);
   SignMfmaArgs a = args;
   a.tiles_per_split = static_cast<int>(p.tps);
   a.one = 0x3C003C00u;
-  hipLaunchKernelGGL(sign_mfma_kernel<RES>,
-                     dim3(static_cast<unsigned>(p.bands), static_cast<unsigned>(p.mtiles),
-                          static_cast<unsigned>(p.nsplit)),
-                     dim3(256), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(p.cols), static_cast<unsigned>(p.mtiles),
+                  static_cast<unsigned>(p.nsplit));
+  const bool small = p.tps <= 4 * kStWaves;   // at most four tiles per wave
+  if (p.kernel == 1) {
+    if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4>), grid, dim3(64 * kStWaves), 0, s, a);
+    else hipLaunchKernelGGL((sign_staged_kernel<RES, 1, kStMaxPerWave>), grid, dim3(64 * kStWaves), 0, s, a);
+  } else if constexpr (!RES) {
+    if (p.kernel == 4) {
+      if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 4, 4>), grid, dim3(64 * kStWaves), 0, s, a);
+      else hipLaunchKernelGGL((sign_staged_kernel<RES, 4, kStMaxPerWave>), grid, dim3(64 * kStWaves), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(sign_mfma_kernel<RES>, grid, dim3(256), 0, s, a);
+    }
+  } else
+    hipLaunchKernelGGL(sign_mfma_kernel<RES>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // fp32 partials the kernel needs for a shape under the default plan.
-inline size_t sign_mfma_part_floats(int64_t M, int64_t N, int64_t K) {
-  const SignPlan p = plan_sign_mfma(M, N, K, kSignWgTarget);
+inline size_t sign_mfma_part_floats(int64_t M, int64_t N, int64_t K, bool res) {
+  const SignPlan p = plan_sign_mfma(M, N, K, kSignWgTarget, res);
   return p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * M * N : 0;
 }
 
