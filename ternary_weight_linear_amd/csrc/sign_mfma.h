@@ -502,7 +502,8 @@ inline int64_t sign_wg_target() { return kSignWgTarget; }
 // per wave.
 inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, bool res) {
   const int64_t KT = K / 128, bands = N / 64, mtiles = (M + 15) / 16;
-  const int64_t need = (KT + st_max_tiles(M) - 1) / st_max_tiles(M);   // splits the LDS needs
+  // splits the staged kernel's LDS needs (it serves M <= 4 only)
+  const int64_t need = M <= 4 ? (KT + st_max_tiles(M) - 1) / st_max_tiles(M) : 0;
   int kernel = 0;
   if (M <= 4 && need <= kSignMaxSplits) kernel = bands < target ? 1 : (res ? 0 : 4);
   // a K split needs one counter per workgroup column and 32-bit element offsets

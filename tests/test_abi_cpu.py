@@ -48,6 +48,17 @@ def test_size_queries(lib):
     assert lib.bl_workspace_bytes(0, 64, 64) == 0
 
 
+def test_workspace_sizes_over_shapes(lib):
+    """The host-side launch plans behind bl_workspace_bytes hold for every batch size,
+    including the decode sizes whose sign-plane plan splits K to fit LDS and the prefill
+    sizes that plan never takes."""
+    for M in (1, 2, 3, 4, 5, 16, 17, 64, 512, 4096):
+        for N in (64, 4096, 16384, 28672):
+            for K in (128, 4096, 12288, 65536):
+                ws = lib.bl_workspace_bytes(M, N, K)
+                assert ws > 0 and ws % 256 == 0, (M, N, K)
+
+
 def _p(v):
     return ctypes.c_void_p(v)
 
