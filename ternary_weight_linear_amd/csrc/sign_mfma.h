@@ -296,8 +296,14 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, r16 = lane & 15;
-  const int64_t band = NF == 4 ? blockIdx.x : blockIdx.x >> 2;
-  const int f0 = NF == 4 ? 0 : static_cast<int>(blockIdx.x & 3);
+  // NF = 1: dispatch ids are dealt round-robin over the 8 XCDs (id i runs on XCD i % 8);
+  // ids i, i + 8, i + 16, i + 24 take the four fragments of one band, so they share an XCD
+  // and the band's sign records come from HBM once and from that XCD's L2 three times (with
+  // consecutive ids per band, every fragment missed in its own XCD's L2: 4x the HBM bytes).
+  // The grid is rounded up to 32; ids past the last band have nothing to do.
+  const int64_t band = NF == 4 ? blockIdx.x : (blockIdx.x >> 5) * 8 + (blockIdx.x & 7);
+  const int f0 = NF == 4 ? 0 : static_cast<int>((blockIdx.x >> 3) & 3);
+  if (band >= a.N / 64) return;
   const int split = blockIdx.z, nsplit = gridDim.z;
   const int M = static_cast<int>(a.M);
   const int KT = static_cast<int>(a.K / 128);
@@ -508,10 +514,10 @@ inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, 
   if (M <= 4 && need <= kSignMaxSplits) kernel = bands < target ? 1 : (res ? 0 : 4);
   // a K split needs one counter per workgroup column and 32-bit element offsets
   auto can_split = [&](int k) {
-    return mtiles * (k == 1 ? 4 * bands : bands) <= kMaxCounters && M * N < (int64_t(1) << 30);
+    return mtiles * (k == 1 ? 4 * bands + 31 : bands) <= kMaxCounters && M * N < (int64_t(1) << 30);
   };
   if (kernel != 0 && need > 1 && !can_split(kernel)) kernel = 0;
-  const int64_t cols = kernel == 1 ? 4 * bands : bands;
+  const int64_t cols = kernel == 1 ? (4 * bands + 31) / 32 * 32 : bands;
   const int64_t per_wave = kernel ? kStWaves : 4;
   int64_t nsplit = (target + cols * mtiles - 1) / (cols * mtiles);
   nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / per_wave));
