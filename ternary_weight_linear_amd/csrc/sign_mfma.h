@@ -286,8 +286,10 @@ __host__ __device__ constexpr int st_max_tiles(int64_t M) {
 }
 constexpr int kStMaxPerWave = (st_max_tiles(1) + kStWaves - 1) / kStWaves;
 // PW: tiles per wave the kernel is built for (4 or kStMaxPerWave): every one of them is
-// loaded (clamped into the range), so short ranges take the small build.
-template <bool RES, int NF, int PW>
+// loaded (clamped into the range), so short ranges take the small build. XG (5..16 rows of x):
+// x is not staged but loaded per tile into registers with the sign words (lanes of rows past
+// M load row M - 1), only g goes through LDS; built for PW = 4.
+template <bool RES, int NF, int PW, bool XG>
 __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMfmaArgs a) {
   constexpr int kPad = 68;
   static_assert(kStWaves * 4 * NF * kPad * 4 <= kStLdsBytes, "reduction fits the staging buffer");
@@ -314,19 +316,26 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
   // 1. issue the staging loads (x rows, then g), then every sign word of this wave's tiles.
   // Every load is unconditional (indices past the range are clamped into it): loads under
   // branches made the compiler wait for each one before issuing the next.
-  const int xpieces = M * nt * 16, npieces = xpieces + (RES ? 0 : nt * 16);
+  static_assert(!XG || PW == 4, "registers: x of four tiles per wave");
+  constexpr bool kStage = !(XG && RES);                 // anything to stage in LDS
+  const int Ms = XG ? 0 : M;                            // rows of x staged
+  const int xpieces = Ms * nt * 16, npieces = xpieces + (RES ? 0 : nt * 16);
   sm_u32x4 sv[kStStage];
+  if constexpr (kStage) {
 #pragma unroll
-  for (int i = 0; i < kStStage; ++i) {
-    const int pc = min(tid + 64 * kStWaves * i, npieces - 1);
-    const int m = pc / (nt * 16), q = pc - m * nt * 16;   // m == M: g
-    const uint16_t* src = m < M ? a.x + static_cast<int64_t>(m) * a.K : a.g;
-    sv[i] = *reinterpret_cast<const sm_u32x4*>(src + static_cast<int64_t>(t0) * 128 + 8 * q);
+    for (int i = 0; i < kStStage; ++i) {
+      const int pc = min(tid + 64 * kStWaves * i, npieces - 1);
+      const int m = pc / (nt * 16), q = pc - m * nt * 16;   // m == Ms: g
+      const uint16_t* src = m < Ms ? a.x + static_cast<int64_t>(m) * a.K : a.g;
+      sv[i] = *reinterpret_cast<const sm_u32x4*>(src + static_cast<int64_t>(t0) * 128 + 8 * q);
+    }
   }
   const int first = t0 + wave;
   const int n = first < t1 ? (t1 - first + kStWaves - 1) / kStWaves : 0;
   uint32_t w0[PW][NF], w1[RES ? PW : 1][NF];
   float c0[RES ? PW : 1][NF], c1[RES ? PW : 1][NF];
+  sm_u32x4 xv[XG ? PW : 1][4];
+  const uint16_t* xg_row = a.x + static_cast<int64_t>(min(r16, M - 1)) * a.K + 8 * grp;
   const uint32_t soff = 16u * lane + 4u * static_cast<uint32_t>(f0);
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
@@ -347,6 +356,11 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
         w0[j][0] = sm_load<uint32_t>(rec0, soff);
         if constexpr (RES) w1[j][0] = sm_load<uint32_t>(rec1, soff);
       }
+      if constexpr (XG) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+          xv[j][sl] = *reinterpret_cast<const sm_u32x4*>(xg_row + static_cast<int64_t>(t) * 128 + 32 * sl);
+      }
       if constexpr (RES) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -358,16 +372,18 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
     }
   }
   // 2. staged pieces to LDS: x row m at m * nt * 128 halves, g after the M rows
+  if constexpr (kStage) {
 #pragma unroll
-  for (int i = 0; i < kStStage; ++i) {
-    const int pc = tid + 64 * kStWaves * i;
-    if (pc < npieces) *reinterpret_cast<sm_u32x4*>(st + 8 * pc) = sv[i];
+    for (int i = 0; i < kStStage; ++i) {
+      const int pc = tid + 64 * kStWaves * i;
+      if (pc < npieces) *reinterpret_cast<sm_u32x4*>(st + 8 * pc) = sv[i];
+    }
   }
   __syncthreads();
 
   // 3. products: lane (grp, r16) feeds row min(r16, M - 1) of x and column 16 f + r16
   const uint16_t* xrow = st + static_cast<int64_t>(min(r16, M - 1)) * nt * 128 + 8 * grp;
-  const uint16_t* grow = st + static_cast<int64_t>(M) * nt * 128 + 8 * grp;
+  const uint16_t* grow = st + static_cast<int64_t>(Ms) * nt * 128 + 8 * grp;
   sm_f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = sm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -382,7 +398,9 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
       }
       auto slice = [&](auto sc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
-        const sm_f16x8 av = *reinterpret_cast<const sm_f16x8*>(xrow + tl * 128 + 32 * S);
+        sm_f16x8 av;
+        if constexpr (XG) av = __builtin_bit_cast(sm_f16x8, xv[j][S]);
+        else av = *reinterpret_cast<const sm_f16x8*>(xrow + tl * 128 + 32 * S);
         if constexpr (!RES) {
           const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
 #pragma unroll
@@ -491,27 +509,31 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
 }
 
 // kernel: 0 = band kernel (sign_mfma_kernel), 1 = staged kernel with one fragment per
-// workgroup, 4 = staged kernel with one band per workgroup.
-struct SignPlan { int64_t cols, mtiles, nsplit, tps; int kernel; };
+// workgroup, 4 = staged kernel with one band per workgroup; xg: x loaded per tile (5..16 rows).
+struct SignPlan { int64_t cols, mtiles, nsplit, tps; int kernel; bool xg; };
 
 // Workgroups to aim for. Tuning harnesses that compile the sources directly may set it
 // (0 = the default); the workspace is sized for the default.
 constexpr int64_t kSignWgTarget = 256;
 inline int64_t sign_wg_target() { return kSignWgTarget; }
 
-// Decode-sized batches (M <= 4) take the staged kernel: one fragment per workgroup where
-// the bands alone leave the chip short of `target` workgroups, one band per workgroup
-// otherwise (OneBit only: the residual's two planes and scales would not fit the registers of
-// a deep burst). K is split across workgroups while the workgroups still fall short of
-// `target`, and for the staged kernel also where a range would not fit its LDS (at most
-// kSignMaxSplits splits; beyond that the band kernel); each split keeps at least one tile
-// per wave.
+// Decode-sized batches (M <= 16) take the staged kernel: one fragment per workgroup where
+// the bands leave the chip short of `target` workgroups; at M <= 4 (x staged in LDS) one band
+// per workgroup otherwise (OneBit only: the residual's two planes and scales would not fit the
+// registers of a deep burst); else the band kernel. K is split across workgroups while the
+// workgroups still fall short of `target`, and for the staged kernel also where a range would
+// not fit (its LDS at M <= 4, four tiles per wave above); at most kSignMaxSplits splits, beyond
+// that the band kernel. Each split keeps at least one tile per wave.
 inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, bool res) {
   const int64_t KT = K / 128, bands = N / 64, mtiles = (M + 15) / 16;
-  // splits the staged kernel's LDS needs (it serves M <= 4 only)
-  const int64_t need = M <= 4 ? (KT + st_max_tiles(M) - 1) / st_max_tiles(M) : 0;
+  const bool xg = M > 4;
+  int64_t need = 0;   // splits the staged kernel's range bound needs
   int kernel = 0;
-  if (M <= 4 && need <= kSignMaxSplits) kernel = bands < target ? 1 : (res ? 0 : 4);
+  if (M <= 16) {
+    const int64_t cap = xg ? 4 * kStWaves : st_max_tiles(M);
+    need = (KT + cap - 1) / cap;
+    if (need <= kSignMaxSplits) kernel = bands < target ? 1 : (res || xg ? 0 : 4);
+  }
   // a K split needs one counter per workgroup column and 32-bit element offsets
   auto can_split = [&](int k) {
     return mtiles * (k == 1 ? 4 * bands + 31 : bands) <= kMaxCounters && M * N < (int64_t(1) << 30);
@@ -525,7 +547,7 @@ inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, 
   nsplit = std::min<int64_t>(std::max<int64_t>(nsplit, 1), kSignMaxSplits);
   if (!can_split(kernel)) nsplit = 1;
   const int64_t tps = (KT + nsplit - 1) / nsplit;
-  return {cols, mtiles, (KT + tps - 1) / tps, tps, kernel};
+  return {cols, mtiles, (KT + tps - 1) / tps, tps, kernel, kernel != 0 && xg};
 }
 
 template <bool RES>
@@ -536,19 +558,22 @@ inline hipError_t launch_sign_mfma(const SignMfmaArgs& args, hipStream_t s) {
   a.one = 0x3C003C00u;
   const dim3 grid(static_cast<unsigned>(p.cols), static_cast<unsigned>(p.mtiles),
                   static_cast<unsigned>(p.nsplit));
+  const dim3 block(64 * kStWaves);
   const bool small = p.tps <= 4 * kStWaves;   // at most four tiles per wave
   if (p.kernel == 1) {
-    if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4>), grid, dim3(64 * kStWaves), 0, s, a);
-    else hipLaunchKernelGGL((sign_staged_kernel<RES, 1, kStMaxPerWave>), grid, dim3(64 * kStWaves), 0, s, a);
+    if (p.xg) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4, true>), grid, block, 0, s, a);
+    else if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sign_staged_kernel<RES, 1, kStMaxPerWave, false>), grid, block, 0, s, a);
   } else if constexpr (!RES) {
     if (p.kernel == 4) {
-      if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 4, 4>), grid, dim3(64 * kStWaves), 0, s, a);
-      else hipLaunchKernelGGL((sign_staged_kernel<RES, 4, kStMaxPerWave>), grid, dim3(64 * kStWaves), 0, s, a);
+      if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 4, 4, false>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((sign_staged_kernel<RES, 4, kStMaxPerWave, false>), grid, block, 0, s, a);
     } else {
       hipLaunchKernelGGL(sign_mfma_kernel<RES>, grid, dim3(256), 0, s, a);
     }
-  } else
+  } else {
     hipLaunchKernelGGL(sign_mfma_kernel<RES>, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -371,7 +371,8 @@ def _onebit_inputs(M, N, K, seed=0):
                                    (5, 320, 384), (1, 4096, 4096), (16, 4096, 4096), (3, 448, 1024),
                                    (4, 256, 640), (33, 192, 512), (17, 1024, 8192),
                                    (1, 512, 8192), (1, 16384, 256), (2, 16384, 384),
-                                   (4, 16384, 5120), (1, 2048, 12288)])
+                                   (4, 16384, 5120), (1, 2048, 12288), (8, 1024, 8192),
+                                   (12, 16384, 256)])
 def test_onebit(M, N, K):
     """Covers the three workgroup mappings: at M <= 4 one 16-column fragment per workgroup
     (few bands; (1, 512, 8192) also splits K) or one band per workgroup with x and g staged
@@ -494,7 +495,7 @@ def test_residual_binarize(N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 4096, 4096), (2, 320, 384), (3, 192, 1280),
                                    (5, 448, 1024), (16, 512, 512), (17, 1024, 8192),
                                    (33, 192, 512), (64, 256, 2048), (1, 256, 4096),
-                                   (2, 16384, 256), (1, 2048, 12288)])
+                                   (2, 16384, 256), (1, 2048, 12288), (12, 1024, 8192)])
 def test_residual_linear(M, N, K):
     """Forward on planes and scales packed by the oracle (independent of the GPU packer)."""
     say("residual_linear", M, N, K)
