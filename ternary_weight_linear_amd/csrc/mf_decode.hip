@@ -80,8 +80,8 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
   auto load_batch = [&](u32x4 (&dst)[kMBatch], int rel) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kMBatch; ++t)
-      dst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wr, (rel + t) * 1024 + lane * 16, 0, 0));
+      dst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(   // nt: read once
+                                             wr, (rel + t) * 1024 + lane * 16, 0, 2));
     __builtin_amdgcn_sched_barrier(0);   // keep each batch where it is issued
   };
 

@@ -293,7 +293,8 @@ __global__ __launch_bounds__(64 * kSW) void gemv_stack_kernel(StackHeader* __res
   auto issue = [&](u32x4 (&dst)[kSB], const Cursor& c) __attribute__((always_inline)) {
     const auto wp = band_ptr(c);
 #pragma unroll
-    for (int u = 0; u < kSB; ++u) dst[u] = wp[static_cast<int64_t>(min(c.t + u, c.cend - 1)) * 64];
+    for (int u = 0; u < kSB; ++u)   // weights are read once: non-temporal
+      dst[u] = __builtin_nontemporal_load(&wp[static_cast<int64_t>(min(c.t + u, c.cend - 1)) * 64]);
   };
 
   float gam[MR];
