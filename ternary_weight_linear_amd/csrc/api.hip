@@ -369,10 +369,12 @@ int bl_bitlinear_forward_mf(const uint16_t* x, int64_t M, int64_t K, const void*
   char* w = static_cast<char*>(ws);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   // decode: one launch quantises and multiplies. Each workgroup quantises its K range of
-  // every row itself, so beyond two rows that pays only where few workgroups share a range
-  // (measured on MI355X, 70B-shaped linears at M = 8: 10 % faster than quantiser + product
-  // launches for q|k|v and o, 20-35 % slower for gate|up and down)
-  if (mf_decode_fits(M, N, K) && (M <= 2 || (K <= 8192 && N / 64 < 512)))
+  // every row itself, so beyond four rows that pays only for narrow outputs of short rows
+  // (measured on MI355X, 70B-shaped linears, us per call: M = 4 all four shapes fused, e.g.
+  // down 18.7 against 20.0 for quantiser + product; M = 8 q|k|v 13.1 / o 12.3 fused against
+  // 14.6 / 14.4, gate|up 32.3 against 27.7, down 23.4 against 23.0; M = 16 q|k|v and o
+  // 19.6 / 18.5 against 19.6 / 17.8, down 45.8 against 28.3)
+  if (mf_decode_fits(M, N, K) && (M <= 4 || (K <= 8192 && N / 64 < 512)))
     return check_launch(launch_mf_decode(x, static_cast<int>(M), K, wmf, beta, beta_len, N, y,
                                          reinterpret_cast<uint64_t*>(w + L.acc_off), s),
                         "bl_bitlinear_forward_mf");

@@ -115,6 +115,13 @@ bool mf_decode_fits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mf_decode(const uint16_t* x, int M, int64_t K, const void* wmf,
                             const float* beta, int64_t beta_len, int64_t N, float* y,
                             uint64_t* ws_acc, hipStream_t s);
+// The same product from q given (quantiser outputs), M <= 16 where mf_decode_fits; raw int32
+// outputs into acc_out and/or the fp32 epilogue into y.
+bool mf_qgemv_fits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_mf_qgemv(const int8_t* q, const float* gamma, const int32_t* rowsum, int M,
+                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
+                           hipStream_t s);
 hipError_t launch_onebit(const uint16_t* x, const uint16_t* g, const void* spacked,
                          const uint16_t* h, int64_t M, int64_t N, int64_t K, float* y,
                          float* ws_part, uint32_t* ws_cnt, hipStream_t s);
@@ -139,6 +146,41 @@ __device__ __forceinline__ int quant_q(float a, float g, float rg) {
     d = near ? e : d;
   }
   return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d), -127.0f, 127.0f));
+}
+
+// quant_q for N inputs at once (input e of row gamma g[e], rg[e] = rcp(g[e]); zero[e]: the
+// row's gamma is 0 or not finite, q = 0). The distances of the N quotients from the nearest
+// half-integer are folded into one minimum, so one compare and one wave-uniform test cover
+// them all and the common case is straight-line VALU code (quant_q per input under a
+// per-row select compiles into a masked branch per input). A zero row clamps to [0, 0]
+// (med3 of a NaN and two zeros is zero). Same results as quant_q input by input.
+template <int N>
+__device__ __forceinline__ void quant_q_n(const float (&a)[N], const float (&g)[N],
+                                          const float (&rg)[N], const bool (&zero)[N],
+                                          int (&q)[N]) {
+  float d[N], t[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    d[e] = a[e] * rg[e];
+    t[e] = fabsf(__builtin_amdgcn_fractf(d[e]) - 0.5f);
+  }
+  float tmin = t[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) tmin = fminf(tmin, t[e]);
+  if (__ballot(tmin < 0x1p-12f) != 0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      float gv = g[e];
+      asm volatile("" : "+v"(gv));   // keeps the division inside the branch
+      const float div = a[e] / gv;
+      d[e] = t[e] < 0x1p-12f ? div : d[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float lim = zero[e] ? 0.0f : 127.0f;
+    q[e] = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(d[e]), -lim, lim));
+  }
 }
 
 // Maximum over the 64 lanes of a wave, returned to every lane: DPP steps within quads,
@@ -245,6 +287,45 @@ __device__ __forceinline__ uint32_t split_arrive_batch(WordFn word, int32_t (&v)
     if (((active >> e) & 1u) && (now[e] >> 32) == static_cast<uint64_t>(nsplit)) {
       v[e] = static_cast<int32_t>(static_cast<uint32_t>(now[e]) -
                                   static_cast<uint32_t>(nsplit) * static_cast<uint32_t>(kSplitOffset));
+      __hip_atomic_store(word(e), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last |= 1u << e;
+    }
+  }
+  return last;
+}
+
+// split_arrive_batch for two outputs per word (output pair e = elements 2e, 2e + 1 of v), for
+// at most kMaxPairSplits partials of |p| < kSplitOffset: the word holds the arrival count
+// in bits 54.., and the two sums of (partial + kSplitOffset) in bits 27..53 and 0..26 (each
+// below 8 * 2^24 = 2^27, so neither carries into the next field). Half the atomics of one
+// word per output, still one round trip. Bit e of `active`: pair e takes part (both of its
+// elements are added; an unused second element adds a bias nobody reads); word(e) must be
+// valid for every e. Returns bit e set where this lane completed pair e, v[2e] and v[2e + 1]
+// then holding the exact totals (and the word cleared).
+constexpr int kMaxPairSplits = 8;
+template <int kP, class WordFn>
+__device__ __forceinline__ uint32_t split_arrive_pairs(WordFn word, int32_t (&v)[2 * kP],
+                                                       uint32_t active, int nsplit) {
+  if (active == 0) return 0;
+  constexpr uint64_t kField = (uint64_t(1) << 27) - 1;
+  uint64_t now[kP];
+#pragma unroll
+  for (int e = 0; e < kP; ++e) {
+    const uint64_t add =
+        ((active >> e) & 1u)
+            ? (uint64_t(1) << 54) |
+                  (static_cast<uint64_t>(static_cast<uint32_t>(v[2 * e + 1] + kSplitOffset)) << 27) |
+                  static_cast<uint64_t>(static_cast<uint32_t>(v[2 * e] + kSplitOffset))
+            : uint64_t(0);
+    now[e] = __hip_atomic_fetch_add(word(e), add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+  }
+  uint32_t last = 0;
+  const uint32_t bias = static_cast<uint32_t>(nsplit) * static_cast<uint32_t>(kSplitOffset);
+#pragma unroll
+  for (int e = 0; e < kP; ++e) {
+    if (((active >> e) & 1u) && (now[e] >> 54) == static_cast<uint64_t>(nsplit)) {
+      v[2 * e] = static_cast<int32_t>(static_cast<uint32_t>(now[e] & kField) - bias);
+      v[2 * e + 1] = static_cast<int32_t>(static_cast<uint32_t>((now[e] >> 27) & kField) - bias);
       __hip_atomic_store(word(e), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last |= 1u << e;
     }

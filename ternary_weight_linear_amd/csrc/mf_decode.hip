@@ -49,8 +49,38 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit elements
 // q of a workgroup's whole K range sits in LDS: at most kMaxTiles(MR) tiles (48 KiB).
 template <int MR>
 constexpr int mfd_max_tiles() { return 48 * 1024 / (MR * 64); }
-constexpr int kXR = 2;     // quantisation steps whose x is loaded before the weights
+// quantisation steps whose x is loaded with the first weights (more where a range holds
+// many rows: each later step waits for loads of its own)
+constexpr int mfd_xr(int MR) { return MR >= 8 ? 8 : 2; }
 constexpr int kPre = 1;    // weight batches issued before gamma is folded
+
+// Split-K hand-off of a lane's MR outputs (rows m < M, bit m of `live`, one column): one
+// split word per output, or per pair of rows where the split count allows (half the
+// atomics). Returns the rows whose totals this lane completed (then in v).
+template <int MR>
+__device__ __forceinline__ uint32_t hand_over(int32_t (&v)[MR], uint32_t live, int M, int64_t N,
+                                              int64_t col, uint64_t* ws_acc, int nsplit) {
+  if (nsplit == 1) return live;
+  if constexpr (MR >= 2) {
+    if (nsplit <= kMaxPairSplits) {
+      constexpr int kP = MR / 2;
+      const int pairs = (M + 1) / 2;
+      auto pword = [&](int e) __attribute__((always_inline)) {
+        return ws_acc + static_cast<int64_t>(min(e, pairs - 1)) * N + col;
+      };
+      const uint32_t pd = split_arrive_pairs<kP>(pword, v, (1u << pairs) - 1, nsplit);
+      uint32_t done = 0;
+#pragma unroll
+      for (int e = 0; e < kP; ++e)
+        if ((pd >> e) & 1u) done |= 3u << (2 * e);
+      return done & live;
+    }
+  }
+  auto word = [&](int m) __attribute__((always_inline)) {
+    return ws_acc + static_cast<int64_t>(min(m, M - 1)) * N + col;
+  };
+  return split_arrive_batch<MR>(word, v, live, nsplit);
+}
 
 template <int MR, int GL>
 __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
@@ -58,6 +88,7 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
     const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
     uint64_t* __restrict__ ws_acc, int tiles_per_split) {
   constexpr int kMaxTiles = mfd_max_tiles<MR>();
+  constexpr int kXR = mfd_xr(MR);
   __shared__ __attribute__((aligned(16))) int8_t qb[kMaxTiles * MR * 64];
   __shared__ uint32_t red_max[kMW][MR];
   __shared__ int rsum[MR];
@@ -185,12 +216,15 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
     // p = r % kQR, a constant at every call
     const int row = unit_row(r), tt = unit_tt(r);
     const uint32_t h[4] = {xr.x, xr.y, xr.z, xr.w};
+    float a[8], ge[8], rge[8];
+    bool ze[8];
     int q[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t hb = static_cast<uint16_t>(h[e / 2] >> (16 * (e % 2)));
-      q[e] = qz[p] ? 0 : quant_q(half_bits_to_float(hb) * 127.0f, qg[p], qrg[p]);
+      a[e] = half_bits_to_float(static_cast<uint16_t>(h[e / 2] >> (16 * (e % 2)))) * 127.0f;
+      ge[e] = qg[p], rge[e] = qrg[p], ze[e] = qz[p];
     }
+    quant_q_n(a, ge, rge, ze, q);
     // bytes in input order: perm picks the low byte of each 16-bit half
     const uint32_t d0 = __builtin_amdgcn_perm(
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(q[2], q[3])),
@@ -291,10 +325,7 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
     v[m] = got;
     if (m < M) live |= 1u << m;
   }
-  auto word = [&](int m) __attribute__((always_inline)) {
-    return ws_acc + static_cast<int64_t>(min(m, M - 1)) * N + col;
-  };
-  const uint32_t done = nsplit > 1 ? split_arrive_batch<MR>(word, v, live, nsplit) : live;
+  const uint32_t done = hand_over<MR>(v, live, M, N, col, ws_acc, nsplit);
   const float b = beta[beta_len == 1 ? 0 : col];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -303,6 +334,125 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
     bool zero;
     row_gamma(m, gam, rg, zero);
     y[m * N + col] = static_cast<float>(v[m]) * (gam / 127.0f) * b;
+  }
+}
+
+// The same product with q given (int8 [M, K], gamma [M], rowsum [M] from the quantiser):
+// the workgroup copies q of its K range into LDS (QL 16-byte loads per thread, issued
+// before the weights, addresses past the copy clamped), streams its four bands through the
+// register ring as above, and hands the raw fragment sums to the split words; the workgroup
+// completing an output takes the row's whole-K sum of q away once (fragments f < 3), so no
+// per-range sums are needed.
+template <int MR, int QL>
+__global__ __launch_bounds__(64 * kMW) void mf_qgemv_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ gamma,
+    const int32_t* __restrict__ rowsum, int M, int64_t K, const u32x4* __restrict__ W,
+    const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, uint64_t* __restrict__ ws_acc, int tiles_per_split) {
+  constexpr int kMaxTiles = mfd_max_tiles<MR>();
+  __shared__ __attribute__((aligned(16))) int8_t qb[kMaxTiles * MR * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, u = lane & 15;
+  const int64_t nbands = N / 64;
+  const int64_t band = static_cast<int64_t>(blockIdx.x) * kMW + wave;
+  const bool active = band < nbands;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int KT = static_cast<int>(K / 64);
+  const int t0 = split * tiles_per_split;
+  const int t1 = min(KT, t0 + tiles_per_split);   // t1 - t0 <= kMaxTiles (host plan)
+
+  // the epilogue's row sums and scales, lane l holding row min(l, M - 1) (read back with
+  // readlane), loaded first so that no load waits at the end
+  const int rs_l = rowsum[min(lane, M - 1)];
+  const float gs_l = y != nullptr ? gamma[min(lane, M - 1)] / 127.0f : 0.0f;
+  // q of the range: unit i = (tile i / (4 M), row (i / 4) % M, 16-byte piece i % 4); the
+  // host picks QL with QL * 256 >= the range's units
+  const int units = (t1 - t0) * M * 4;
+  u32x4 qv[QL];
+#pragma unroll
+  for (int l = 0; l < QL; ++l) {
+    const int i = min(tid + 64 * kMW * l, units - 1);
+    const int tile = i / (4 * M), row = (i >> 2) % M;
+    qv[l] = *reinterpret_cast<const u32x4*>(q + static_cast<int64_t>(row) * K +
+                                             static_cast<int64_t>(t0 + tile) * 64 + 16 * (i & 3));
+  }
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(W + ((active ? band : 0) * KT + t0) * 64), 0,
+      active && t1 > t0 ? (t1 - t0) * 1024 : 0, kRsrcWord3);
+  u32x4 w[kMRing][kMBatch];
+  auto load_batch = [&](u32x4 (&dst)[kMBatch], int rel) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kMBatch; ++t)
+      dst[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(   // nt: read once
+                                             wr, (rel + t) * 1024 + lane * 16, 0, 2));
+    __builtin_amdgcn_sched_barrier(0);   // keep each batch where it is issued
+  };
+#pragma unroll
+  for (int r = 0; r < kMRing; ++r) load_batch(w[r], r * kMBatch);
+#pragma unroll
+  for (int l = 0; l < QL; ++l) {
+    const int i = tid + 64 * kMW * l;
+    if (i < units) {
+      const int tile = i / (4 * M), row = (i >> 2) % M;
+      *reinterpret_cast<u32x4*>(&qb[(tile * MR + row) * 64 + 16 * (i & 3)]) = qv[l];
+    }
+  }
+  __syncthreads();
+
+  i32x4 acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) acc[f] = i32x4{0, 0, 0, 0};
+  const int rowu = min(u, M - 1);   // A operand row of this lane (M <= MR)
+  if (!active) return;
+  for (int tb = t0; tb < t1; tb += kMRing * kMBatch) {
+#pragma unroll
+    for (int r = 0; r < kMRing; ++r) {
+      const int tr = tb + r * kMBatch;
+      if (tr < t1) {   // tiles past the range hold zero weights; their q index is clamped
+#pragma unroll
+        for (int t = 0; t < kMBatch; ++t) {
+          const int pt = min(tr + t - t0, kMaxTiles - 1);
+          const i32x4 av = *reinterpret_cast<const i32x4*>(&qb[(pt * MR + rowu) * 64 + 16 * g]);
+          const uint32_t w4[4] = {w[r][t].x, w[r][t].y, w[r][t].z, w[r][t].w};
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            i32x4 b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = static_cast<int>(w4[j] & (0x03030303u << (2 * f)));
+            acc[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, acc[f], 0, 0, 0);
+          }
+        }
+      }
+      load_batch(w[r], tr - t0 + kMRing * kMBatch);
+    }
+  }
+  // outputs to lane = column (as above); raw fragment sums, at most MR per lane
+  const int64_t col = band * 64 + lane;
+  int32_t v[MR];
+  uint32_t live = 0;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int src = (16 * (m >> 2) + (lane & 15)) * 4;
+    int got = 0;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int t = __builtin_amdgcn_ds_bpermute(src, acc[f][m & 3] >> (2 * f));
+      got = (lane >> 4) == f ? t : got;
+    }
+    v[m] = got;
+    if (m < M) live |= 1u << m;
+  }
+  const uint32_t done = hand_over<MR>(v, live, M, N, col, ws_acc, nsplit);
+  const float b = y != nullptr ? beta[beta_len == 1 ? 0 : col] : 0.0f;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (!((done >> m) & 1u)) continue;
+    const int r = v[m] - (lane < 48 ? __builtin_amdgcn_readlane(rs_l, m) : 0);   // f < 3: q (w + 1)
+    if (acc_out) acc_out[m * N + col] = r;
+    if (y)
+      y[m * N + col] = static_cast<float>(r) *
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs_l), m)) * b;
   }
 }
 
@@ -343,6 +493,38 @@ MfdPlan plan_mf_decode(int M, int64_t N, int64_t K) {
 
 bool mf_decode_fits(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && K <= 32768 && plan_mf_decode(static_cast<int>(M), N, K).groups > 0;
+}
+
+bool mf_qgemv_fits(int64_t M, int64_t N, int64_t K) { return mf_decode_fits(M, N, K); }
+
+hipError_t launch_mf_qgemv(const int8_t* q, const float* gamma, const int32_t* rowsum, int M,
+                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
+                           hipStream_t s) {
+  if (!mf_qgemv_fits(M, N, K)) return hipErrorInvalidValue;
+  const MfdPlan p = plan_mf_decode(M, N, K);
+  const dim3 grid(static_cast<unsigned>(p.groups), static_cast<unsigned>(p.nsplit));
+  const u32x4* W = static_cast<const u32x4*>(wmf);
+  // 16-byte pieces of q per workgroup: <= 4 per thread (copy of up to 1024), else <= 12
+  // (the LDS bound: kMaxTiles(MR) * MR * 4 = 3072 pieces)
+  const bool few = p.tps * M * 4 <= 64 * kMW * 4;
+#define BL_MFQ2(MR_, QL_)                                                                   \
+  hipLaunchKernelGGL((mf_qgemv_kernel<MR_, QL_>), grid, dim3(64 * kMW), 0, s, q, gamma,   \
+                     rowsum, M, K, W, beta, beta_len, N, y, acc_out, ws_acc,               \
+                     static_cast<int>(p.tps))
+#define BL_MFQ(MR_)               \
+  do {                            \
+    if (few) BL_MFQ2(MR_, 4);     \
+    else BL_MFQ2(MR_, 12);        \
+  } while (0)
+  if (M == 1) BL_MFQ(1);
+  else if (M == 2) BL_MFQ(2);
+  else if (M <= 4) BL_MFQ(4);
+  else if (M <= 8) BL_MFQ(8);
+  else BL_MFQ(16);
+#undef BL_MFQ
+#undef BL_MFQ2
+  return hipGetLastError();
 }
 
 hipError_t launch_mf_decode(const uint16_t* x, int M, int64_t K, const void* wmf,

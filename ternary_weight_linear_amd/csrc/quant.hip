@@ -146,13 +146,20 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
     const int64_t i = threadIdx.x + BLOCK * n;
     if (i >= K8) break;
     const uint32_t w[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+    float a[8], ge[8], rge[8];
+    bool ze[8];
+    int qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = half_bits_to_float(static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu)) * 127.0f;
+      ge[e] = g, rge[e] = rg, ze[e] = zero;
+    }
+    quant_q_n(a, ge, rge, ze, qv);
     uint32_t packed[2] = {0, 0};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t hb = static_cast<uint16_t>((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      const int qv = zero ? 0 : quant_q(half_bits_to_float(hb) * 127.0f, g, rg);
-      sum += qv;
-      packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * (e & 3));
+      sum += qv[e];
+      packed[e >> 2] |= (static_cast<uint32_t>(qv[e]) & 0xFFu) << (8 * (e & 3));
     }
     if (q) *reinterpret_cast<uint2*>(q + m * K + 8 * i) = make_uint2(packed[0], packed[1]);
   }

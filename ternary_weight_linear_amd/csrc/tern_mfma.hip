@@ -658,6 +658,13 @@ hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* ro
   // so that it fills the GPU without splitting K (e.g. gate|up at M = 64: 42 us against 91
   // us per band; every 3B GEMM at M = 512); with fewer, K splits would cost M x N
   // split-word atomics per split, more than the per-band kernel's repeated weight reads
+  // up to eight rows of narrow outputs: the four-band kernel with q of a whole K range in
+  // LDS (measured on MI355X, 70B-shaped, us: M = 8 q|k|v 11.4 / o 11.0 / down 17.4
+  // against 13.3 / 12.2 / 19.6 here; M = 1 down 13.3 against 16.0; wide outputs and M = 16
+  // were slower, e.g. gate|up at M = 8 27.6 against 23.9)
+  if (M <= 8 && N / 64 < 512 && mf_qgemv_fits(M, N, K))
+    return launch_mf_qgemv(q, gamma, rowsum, static_cast<int>(M), K, wmf, beta, beta_len, N, y,
+                           acc_out, ws_acc, s);
   const int64_t groups = (N / 64 + 3) / 4;
   const int64_t items = groups * ((M + 16 * mfq_fm(M, groups) - 1) / (16 * mfq_fm(M, groups)));
   const bool quad = items >= 160;

@@ -759,11 +759,17 @@ def test_mf_invalid_codes():
     assert np.array_equal(host(mf2), oracle.pack_ternary_mf(np.zeros((64, 64), dtype=np.int8)))
 
 
-# Four-band groups x row tiles >= 160 take the staged-q kernel (N = 49152, 10240 at M = 200),
+# Up to eight rows over fewer than 512 bands take the four-band kernel with q of a K range
+# in LDS: no split (1 x 64 x 64, 1 x 128 x 256), split words per output (more than eight
+# splits: 5 x 192 x 320) or per pair of rows (7 x 10240 x 8192 and 3 x 8192 x 28672: odd M,
+# the last pair half unused; 8 x 8192 x 28672), a ragged last group of 511 bands. Otherwise
+# four-band groups x row tiles >= 160 take the staged-q kernel (N = 49152, 10240 at M = 200),
 # fewer the per-band one; 49216 leaves a last group with one band; M = 40, 70, 200 ragged
 # row tiles; M >= 256 over >= 32 band groups the 48-row tiles (300 = 6 x 48 + 12), with a
 # K split past 32768 inputs (256 x 8192 x 33792).
-@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 192, 320), (8, 512, 512), (16, 640, 1024),
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 128, 256), (5, 192, 320), (8, 512, 512),
+                                   (7, 10240, 8192), (3, 8192, 28672), (8, 32704, 4096),
+                                   (16, 640, 1024),
                                    (17, 384, 448), (33, 256, 640), (64, 1024, 8192),
                                    (100, 256, 640), (2, 128, 39936), (8, 8192, 28672),
                                    (1, 49216, 64), (8, 49152, 256), (40, 49152, 192),
@@ -796,18 +802,22 @@ def test_gemm_mf_acc_and_output(M, N, K):
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
 
 
-# Decode through T2-MF64. The fused kernel takes M <= 2, and M <= 16 where K <= 8192 and
-# the output has < 512 bands; the other shapes go through quantiser + product. Fused
+# Decode through T2-MF64. The fused kernel takes M <= 4, and M <= 16 where K <= 8192 and
+# the output has < 512 bands; the other shapes go through quantiser + product (the four-band
+# q-in-LDS kernel up to eight rows over < 512 bands: 6 x 8192 x 28672; the staged-q or
+# per-band kernels beyond: 12 x 8192 x 28672). Fused: M = 4 over the 70B down shape (eight
+# splits, split words per pair of rows), M = 8 over q|k|v. Fused
 # shapes: one tile; ragged band groups (inactive waves) with long rows (row loads past 8192
 # inputs); the largest K; long K ranges per workgroup (K split in two over wide outputs);
 # no K split (>= 512 band groups at M = 1; a 4-tile K at M = 16); ranges past the LDS
 # capacity of 16 rows (more splits); every row-tile width 1, 2, 4, 8, 16 with unused rows.
-# Routed elsewhere: long or wide shapes at M > 2, and M x N past the split words' capacity.
+# Routed elsewhere: long or wide shapes at M > 4, and M x N past the split words' capacity.
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 320, 8256), (2, 128, 28672),
                                    (1, 65536, 16384), (1, 131072, 256), (16, 2048, 256),
                                    (16, 32704, 8192), (8, 32704, 8192), (5, 448, 4160),
                                    (13, 192, 2048), (4, 10240, 8192), (3, 65536, 16384),
-                                   (8, 65536, 8192), (16, 262208, 4096)])
+                                   (8, 65536, 8192), (16, 262208, 4096), (4, 8192, 28672),
+                                   (8, 10240, 8192), (6, 8192, 28672), (12, 8192, 28672)])
 def test_forward_mf_decode_equals_forward(M, N, K):
     """The fused decode kernel gives the outputs of the unfused T2-PN-64 path to the bit and
     matches the oracle on sampled rows."""
