@@ -30,6 +30,7 @@ constexpr int kWaves = 4;
 constexpr int kUnroll = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int MR>
 __global__ __launch_bounds__(256) void gemv_kernel(
@@ -200,10 +201,17 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
   u32x4 gx[MR][GL > 0 ? GL : 1];
   if constexpr (GL > 0) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
+    for (int m = 0; m < MR; ++m) {
+      // row m through a buffer resource of its own: loads past the row read zero, which
+      // leaves the maximum unchanged, and the offset needs no clamp
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(x + static_cast<int64_t>(m) * K), 0, static_cast<int>(K * 2),
+          kRsrcWord3);
 #pragma unroll
-      for (int i = 0; i < GL; ++i)   // repeated elements do not change the maximum
-        gx[m][i] = row4[m * K8 + min<int64_t>(threadIdx.x + 64 * kFW * i, K8 - 1)];
+      for (int i = 0; i < GL; ++i)
+        gx[m][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 xr, (threadIdx.x + 64 * kFW * i) * 16, 0, 0));
+    }
   }
   uint16_t xq[kPerWave][MR];
   load_x(xq, t0, min(t1, t0 + kChunk));
@@ -217,11 +225,13 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
   bool zero[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    uint32_t mb = 0;
+    // both halves at once (packed 16-bit max), then the wave maximum through DPP
+    u16x2 m2 = {0, 0};
     auto fold = [&](const u32x4& v) {
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mb = max(mb, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
+      for (int j = 0; j < 4; ++j)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w4[j] & 0x7FFF7FFFu));
     };
     if constexpr (GL > 0) {
 #pragma unroll
@@ -230,8 +240,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
 #pragma unroll 4
       for (int64_t i = threadIdx.x; i < K8; i += 64 * kFW) fold(row4[m * K8 + i]);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, off)));
+    const uint32_t mb = wave_max_u32(max(static_cast<uint32_t>(m2.x), static_cast<uint32_t>(m2.y)));
     if (lane == 0) red_max[wave][m] = mb;
   }
   __syncthreads();
