@@ -527,11 +527,31 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
       v[k] = acc[fm][k / 4][k % 4] >> (2 * (k / 4));
       if (m0 + 16 * fm + 4 * g + k % 4 < a.M) live |= 1u << k;
     }
-    auto word = [&](int k) __attribute__((always_inline)) {
-      const int64_t row = min<int64_t>(m0 + 16 * fm + 4 * g + k % 4, a.M - 1);
-      return a.ws_acc + row * a.N + band * 64 + 16 * (k / 4) + u;
-    };
-    const uint32_t done = nsplit > 1 ? split_arrive_batch<16>(word, v, live, nsplit) : live;
+    uint32_t done = live;
+    if (nsplit > 1 && nsplit <= kMaxPairSplits) {
+      // rows 4g + 2p and 4g + 2p + 1 of column 16f + u share one split word (pair e = 2f + p
+      // holds outputs k = 2e, 2e + 1), word row = first row / 2
+      uint32_t plive = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (m0 + 16 * fm + 4 * g + 2 * (e & 1) < a.M) plive |= 1u << e;
+      auto pword = [&](int e) __attribute__((always_inline)) {
+        const int64_t r0 = min<int64_t>(m0 + 16 * fm + 4 * g + 2 * (e & 1), a.M - 1);
+        return a.ws_acc + (r0 / 2) * a.N + band * 64 + 16 * (e >> 1) + u;
+      };
+      const uint32_t pd = split_arrive_pairs<8>(pword, v, plive, nsplit);
+      done = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((pd >> e) & 1u) done |= 3u << (2 * e);
+      done &= live;
+    } else if (nsplit > 1) {
+      auto word = [&](int k) __attribute__((always_inline)) {
+        const int64_t row = min<int64_t>(m0 + 16 * fm + 4 * g + k % 4, a.M - 1);
+        return a.ws_acc + row * a.N + band * 64 + 16 * (k / 4) + u;
+      };
+      done = split_arrive_batch<16>(word, v, live, nsplit);
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (!((done >> k) & 1u)) continue;
@@ -617,11 +637,9 @@ int mfq_fm(int64_t M, int64_t groups) {
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 
-// Staged-q kernel: four bands and 16 fm rows per workgroup.
-hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
-                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
-                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
-                          hipStream_t s) {
+struct QuadPlan { int fm; int64_t groups, mgroups, nsplit, tps; };
+
+QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
   const int64_t KT = K / 64, bands = N / 64, groups = (bands + 3) / 4;
   const int fm = mfq_fm(M, groups);
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
@@ -636,7 +654,18 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   if (M * N > kAccCap) nsplit = 1;
   if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
   // (nsplit <= KT / 12 <= 86 < kMaxIntSplits: a split word never overflows its count)
-  const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, tps);
+  return {fm, groups, mgroups, nsplit, tps};
+}
+
+// Staged-q kernel: four bands and 16 fm rows per workgroup.
+hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
+                          int64_t K, const void* wmf, const float* beta, int64_t beta_len,
+                          int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc,
+                          hipStream_t s) {
+  const QuadPlan p = plan_mf_quad(M, N, K);
+  const int fm = p.fm;
+  const int64_t groups = p.groups, mgroups = p.mgroups, nsplit = p.nsplit;
+  const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, p.tps);
   const int64_t nwork = groups * mgroups * nsplit;   // one workgroup per item, 8 | grid
   const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
   if (fm == 1)
@@ -653,11 +682,6 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
 hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* rowsum, int64_t M,
                           int64_t K, const void* wmf, const float* beta, int64_t beta_len,
                           int64_t N, float* y, int32_t* acc_out, uint64_t* ws_acc, hipStream_t s) {
-  // measured on MI355X (70B-shaped decode at M = 8..64, 3B-shaped prefill at M = 512): the
-  // staged-q kernel wherever its work items (four-band groups x row tiles) number >= 160,
-  // so that it fills the GPU without splitting K (e.g. gate|up at M = 64: 42 us against 91
-  // us per band; every 3B GEMM at M = 512); with fewer, K splits would cost M x N
-  // split-word atomics per split, more than the per-band kernel's repeated weight reads
   // up to eight rows of narrow outputs: the four-band kernel with q of a whole K range in
   // LDS (measured on MI355X, 70B-shaped, us: M = 8 q|k|v 11.4 / o 11.0 / down 17.4
   // against 13.3 / 12.2 / 19.6 here; M = 1 down 13.3 against 16.0; wide outputs and M = 16
@@ -665,9 +689,16 @@ hipError_t launch_tern_mf(const int8_t* q, const float* gamma, const int32_t* ro
   if (M <= 8 && N / 64 < 512 && mf_qgemv_fits(M, N, K))
     return launch_mf_qgemv(q, gamma, rowsum, static_cast<int>(M), K, wmf, beta, beta_len, N, y,
                            acc_out, ws_acc, s);
-  const int64_t groups = (N / 64 + 3) / 4;
-  const int64_t items = groups * ((M + 16 * mfq_fm(M, groups) - 1) / (16 * mfq_fm(M, groups)));
-  const bool quad = items >= 160;
+  // otherwise (measured on MI355X, 70B-shaped decode at M = 8..64, 3B-shaped prefill at
+  // M = 512) the staged-q kernel wherever its work items (four-band groups x row tiles)
+  // number >= 160, so that it fills the GPU without splitting K (e.g. gate|up at M = 64:
+  // 42 us against 91 us per band; every 3B GEMM at M = 512), and with fewer where at most
+  // eight K splits meet in split words shared by two rows (M = 64: down 35.3 against 46.7
+  // us per band, q|k|v 18.4 both; M = 32: down 25.1 against 31.4, q|k|v 16.1 against 19.4;
+  // M = 16: down 20.5 against 22.7); more splits would cost M x N split-word atomics per
+  // split, more than the per-band kernel's repeated weight reads
+  const QuadPlan qp = plan_mf_quad(M, N, K);
+  const bool quad = qp.groups * qp.mgroups >= 160 || qp.nsplit <= kMaxPairSplits;
   return quad ? launch_mf_quad(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,
                                ws_acc, s)
               : launch_mf_band(q, gamma, rowsum, M, K, wmf, beta, beta_len, N, y, acc_out,

@@ -760,16 +760,20 @@ def test_mf_invalid_codes():
 
 
 # Up to eight rows over fewer than 512 bands take the four-band kernel with q of a K range
-# in LDS: no split (1 x 64 x 64, 1 x 128 x 256), split words per output (more than eight
-# splits: 5 x 192 x 320) or per pair of rows (7 x 10240 x 8192 and 3 x 8192 x 28672: odd M,
-# the last pair half unused; 8 x 8192 x 28672), a ragged last group of 511 bands. Otherwise
-# four-band groups x row tiles >= 160 take the staged-q kernel (N = 49152, 10240 at M = 200),
-# fewer the per-band one; 49216 leaves a last group with one band; M = 40, 70, 200 ragged
+# in LDS: no split (1 x 64 x 64, 1 x 128 x 256, 5 x 192 x 320), split words per output (more
+# than eight splits: 4 x 256 x 16384, 64 of them) or per pair of rows (7 x 10240 x 8192 and
+# 3 x 8192 x 28672: odd M, the last pair half unused; 8 x 512 x 512, 8 x 8192 x 28672), a
+# ragged last group of 511 bands. Otherwise
+# the staged-q kernel where four-band groups x row tiles >= 160 (N = 49152, 10240 at
+# M = 200) or at most eight K splits meet in split words per pair of rows (64 x 1024 x 8192:
+# eight splits; 33 x 4096 x 8192: four, odd M; 64 x 8192 x 28672: the 70B down projection),
+# the per-band kernel for more splits (2 x 128 x 39936); 49216 leaves a last group with one
+# band; M = 40, 70, 200 ragged
 # row tiles; M >= 256 over >= 32 band groups the 48-row tiles (300 = 6 x 48 + 12), with a
 # K split past 32768 inputs (256 x 8192 x 33792).
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (1, 128, 256), (5, 192, 320), (8, 512, 512),
-                                   (7, 10240, 8192), (3, 8192, 28672), (8, 32704, 4096),
-                                   (16, 640, 1024),
+                                   (4, 256, 16384), (7, 10240, 8192), (3, 8192, 28672), (8, 32704, 4096),
+                                   (33, 4096, 8192), (64, 8192, 28672), (16, 640, 1024),
                                    (17, 384, 448), (33, 256, 640), (64, 1024, 8192),
                                    (100, 256, 640), (2, 128, 39936), (8, 8192, 28672),
                                    (1, 49216, 64), (8, 49152, 256), (40, 49152, 192),
