@@ -204,7 +204,12 @@ def decode_pass_mf(torch, tw, synth, dev, layers_mf, M):
 
     algo_bytes = sum(it["w"].numel() + 2 * M * it["K"] + 4 * M * it["N"] for it in items)
     weight_bytes = sum(it["w"].numel() for it in items)
-    return items, full_pass, algo_bytes, weight_bytes, (1 if M <= 16 else 2) * len(items)
+    # launches per linear, as the header states for bl_bitlinear_forward_mf: one fused launch
+    # at M <= 4, and at M <= 16 for K <= 8192 over fewer than 512 bands; else two
+    def launches(N, K):
+        return 1 if M <= 4 or (M <= 16 and K <= 8192 and N // 64 < 512) else 2
+    return (items, full_pass, algo_bytes, weight_bytes,
+            sum(launches(it["N"], it["K"]) for it in items))
 
 
 def bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, steps, warmup, use_graph=True):
