@@ -490,16 +490,19 @@ def measured_ceilings(torch, dev):
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(0x5A)
+    lib.bl_ceil_stream_read_slices.argtypes = lib.bl_ceil_stream_read.argtypes
     best_read = 0.0
     read_grid = None
-    for grid in (1024, 2048, 4096, 8192):
+    # grid-strided reads, and one contiguous slice per workgroup with non-temporal loads
+    shapes = [("grid-strided", lib.bl_ceil_stream_read, g) for g in (1024, 2048, 4096, 8192)]
+    shapes += [("slices, nt", lib.bl_ceil_stream_read_slices, g) for g in (256, 512, 1024, 2048)]
+    for kind, fn, grid in shapes:
         out = torch.zeros(grid, dtype=torch.int32, device=dev)
         stream = P(torch.cuda.current_stream().cuda_stream)
-        ms = timed(torch, lambda: lib.bl_ceil_stream_read(P(buf.data_ptr()), nbytes, P(out.data_ptr()),
-                                                          grid, stream), 5, 2)
+        ms = timed(torch, lambda: fn(P(buf.data_ptr()), nbytes, P(out.data_ptr()), grid, stream), 5, 2)
         gbs = nbytes / (ms / 1e3) / 1e9
         if gbs > best_read:
-            best_read, read_grid = gbs, grid
+            best_read, read_grid = gbs, f"{kind}, {grid} workgroups"
     del buf
     best_mfma = 0.0
     mfma_grid = None
@@ -512,7 +515,7 @@ def measured_ceilings(torch, dev):
         if tops > best_mfma:
             best_mfma, mfma_grid = tops, grid
     return {"hbm_read_gbs": round(best_read, 1), "hbm_read_frac_spec": round(best_read / HBM_PEAK_GBS, 4),
-            "hbm_read_kernel": f"stream_read_kernel, 4 GiB read once, {read_grid} workgroups",
+            "hbm_read_kernel": f"stream_read_kernel / stream_read_slices_kernel, 4 GiB read once, best: {read_grid}",
             "int8_mfma_tops": round(best_mfma, 1), "int8_mfma_frac_spec": round(best_mfma / INT8_PEAK_TOPS, 4),
             "int8_mfma_kernel": f"mfma_i8_kernel (v_mfma_i32_16x16x64_i8, 8 independent accumulators "
                                 f"per wave), {mfma_grid} workgroups of 4 waves"}

@@ -6,6 +6,9 @@
 //    in flight per thread, grid-strided so consecutive workgroups read consecutive 4 KiB;
 //    the loaded words are folded with XOR into one word per workgroup, so no load can be
 //    removed. Bytes moved = the buffer size.
+//  * bl_ceil_stream_read_slices: the same with each workgroup reading one contiguous slice
+//    of bytes / grid (a multiple of 16 KiB) with non-temporal loads, the access pattern of
+//    the product kernels' weight streams (a workgroup streams its own bands).
 //  * bl_ceil_mfma_i8: v_mfma_i32_16x16x64_i8 on register operands, eight independent
 //    accumulators per wave (the matrix-core pipeline never waits on a result), `iters`
 //    rounds; the accumulators are stored at the end. Ops = 2 * 16 * 16 * 64 per MFMA.
@@ -36,6 +39,23 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   for (; i < n16; i += stride) {
     const u32x4 v = src[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) atomicXor(out + blockIdx.x, acc);
+}
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_slices_kernel(
+    const u32x4* __restrict__ src, int64_t per_wg16, uint32_t* __restrict__ out) {
+  const u32x4* p = src + static_cast<int64_t>(blockIdx.x) * per_wg16;
+  uint32_t acc = 0;
+  for (int64_t i = threadIdx.x; i < per_wg16; i += kReadThreads * kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u)   // per_wg16 is a multiple of 256 * 8: in range
+      v[u] = __builtin_nontemporal_load(p + i + kReadThreads * u);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
@@ -73,6 +93,21 @@ __attribute__((visibility("default"))) int bl_ceil_stream_read(const void* src, 
                                                                void* stream) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kReadThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16,
+                     out);
+  return static_cast<int>(hipGetLastError());
+}
+
+// The same bytes in `grid` contiguous slices, one per workgroup; bytes must be a multiple of
+// grid * 32 KiB. Returns a hipError_t (hipErrorInvalidValue for other sizes).
+__attribute__((visibility("default"))) int bl_ceil_stream_read_slices(const void* src,
+                                                                      int64_t bytes,
+                                                                      uint32_t* out, int grid,
+                                                                      void* stream) {
+  const int64_t slice = grid > 0 ? bytes / grid : 0;
+  if (grid <= 0 || slice * grid != bytes || slice % (kReadThreads * kReadUnroll * 16) != 0)
+    return static_cast<int>(hipErrorInvalidValue);
+  hipLaunchKernelGGL(stream_read_slices_kernel, dim3(grid), dim3(kReadThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), slice / 16,
                      out);
   return static_cast<int>(hipGetLastError());
 }
