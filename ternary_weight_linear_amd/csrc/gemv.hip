@@ -140,7 +140,8 @@ constexpr int kRing = 4;                    // register batches per wave
 constexpr int kChunk = 64;                  // tiles whose planes sit in LDS at once
 constexpr int kFW = 4;                      // waves (bands) per workgroup
 
-static_assert(kChunk % (2 * kRing * kBatch) == 0, "a chunk holds whole ring turns");
+constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chunk
+static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit elements
 // Weights are read once per pass: non-temporal loads (the nt cache policy) keep them from
 // displacing what is reused (x, the split words, outputs). Measured on MI355X, 70B-shaped
@@ -148,22 +149,17 @@ constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit eleme
 constexpr int kLoadNT = 2;
 
 
-// HW waves share each band (HW = 2: eight waves, two per SIMD): wave w takes band w % kFW
-// and every HW-th tile of the range from w / kFW on; their sums meet in LDS at the end.
-template <int MR, int GL, int HW>
-__global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
+template <int MR, int GL>
+__global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
     const uint16_t* __restrict__ x, int64_t K, const u32x4* __restrict__ W,
     const float* __restrict__ beta, int64_t beta_len, int64_t N, float* __restrict__ y,
     uint64_t* __restrict__ ws_acc, uint32_t* __restrict__ ws_cnt, int tiles_per_split) {
-  constexpr int kWaves = kFW * HW;
-  constexpr int kPerWave = kChunk / kWaves;   // tiles each wave quantises per chunk
   __shared__ __attribute__((aligned(16))) uint32_t pl[kChunk][MR][16];
-  __shared__ uint32_t red_max[kWaves][MR];
+  __shared__ uint32_t red_max[kFW][MR];
   const int64_t nbands = N / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hw = wave / kFW;                  // this wave's share of the band's tiles
-  const int64_t band = static_cast<int64_t>(blockIdx.x) * kFW + wave % kFW;
+  const int64_t band = static_cast<int64_t>(blockIdx.x) * kFW + wave;
   const bool active = band < nbands;
   const int split = blockIdx.y;
   const int nsplit = gridDim.y;
@@ -180,14 +176,11 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
   // past it read as zero): branch-free code lets the compiler wait for exactly the loads a
   // step needs instead of for every load in flight.
   u32x4 w[kRing][kBatch];
-  // the wave's tile sequence: tile t0 + hw + HW s for s = 0, 1, ...; a batch holds kBatch
-  // consecutive s
-  auto load_batch = [&](u32x4 (&dst)[kBatch], int sb) {   // s = sb .. sb + kBatch - 1
+  auto load_batch = [&](u32x4 (&dst)[kBatch], int rel) {   // tiles t0 + rel .. + kBatch - 1
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)   // streamed once: non-temporal (aux bit 1, nt)
       dst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wr, (hw + HW * (sb + u)) * 1024 + lane * 16, 0,
-                                             kLoadNT));
+                                             wr, (rel + u) * 1024 + lane * 16, 0, kLoadNT));
     // keep each batch where it is issued: the scheduler would otherwise interleave or sink
     // batches, and the waits for one batch would then cover the next as well
     __builtin_amdgcn_sched_barrier(0);
@@ -195,7 +188,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
   auto load_x = [&](uint16_t (&xq)[kPerWave][MR], int c0, int c1) {
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
-      const int tt = min(c0 + wave + kWaves * j, c1 - 1);
+      const int tt = min(c0 + wave + kFW * j, c1 - 1);
 #pragma unroll
       for (int m = 0; m < MR; ++m) xq[j][m] = x[m * K + 64 * tt + koff];
     }
@@ -217,7 +210,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
 #pragma unroll
       for (int i = 0; i < GL; ++i)
         gx[m][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 xr, (threadIdx.x + 64 * kWaves * i) * 16, 0, 0));
+                                                 xr, (threadIdx.x + 64 * kFW * i) * 16, 0, 0));
     }
   }
   uint16_t xq[kPerWave][MR];
@@ -245,7 +238,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
       for (int i = 0; i < GL; ++i) fold(gx[m][i]);
     } else {
 #pragma unroll 4
-      for (int64_t i = threadIdx.x; i < K8; i += 64 * kWaves) fold(row4[m * K8 + i]);
+      for (int64_t i = threadIdx.x; i < K8; i += 64 * kFW) fold(row4[m * K8 + i]);
     }
     const uint32_t mb = wave_max_u32(max(static_cast<uint32_t>(m2.x), static_cast<uint32_t>(m2.y)));
     if (lane == 0) red_max[wave][m] = mb;
@@ -255,7 +248,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
   for (int m = 0; m < MR; ++m) {
     uint32_t mb = red_max[0][m];
 #pragma unroll
-    for (int w2 = 1; w2 < kWaves; ++w2) mb = max(mb, red_max[w2][m]);
+    for (int w2 = 1; w2 < kFW; ++w2) mb = max(mb, red_max[w2][m]);
     const bool bad = mb >= 0x7C00u;
     g[m] = bad ? __uint_as_float(0x7FC00000u) : half_bits_to_float(static_cast<uint16_t>(mb));
     zero[m] = bad || mb == 0u;
@@ -269,7 +262,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
     for (int b = 0; b < 8; ++b) A[m][b] = 0;
   int cn = 0;
 
-  // quantise tiles c0 + wave + kWaves j of a chunk into LDS; in the first chunk, the ring's
+  // quantise tiles c0 + wave + kFW j of a chunk into LDS; in the first chunk, the ring's
   // remaining batches are issued between the tiles
   auto quantise = [&](int c0, int c1, auto first) {
 #pragma unroll
@@ -277,7 +270,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
       if constexpr (decltype(first)::value) {
         if (j + 1 < kRing) load_batch(w[j + 1], (j + 1) * kBatch);
       }
-      const int tt = c0 + wave + kWaves * j;
+      const int tt = c0 + wave + kFW * j;
       if (tt < c1) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -305,14 +298,13 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
     }
     __syncthreads();
     if (active) {
-      // batch i of the wave's tile sequence sits in ring slot i % kRing; once reduced, the
-      // slot is refilled with batch i + kRing (unconditionally: past the range it reads zero
-      // for free). A chunk holds whole ring turns of every wave's sequence.
-      for (int sb = (c0 - t0) / HW; t0 + hw + HW * sb < c1; sb += kRing * kBatch) {
+      // batch i of the range sits in ring slot i % kRing; once reduced, the slot is refilled
+      // with batch i + kRing (unconditionally: past the range it reads zero for free)
+      for (int tb = c0; tb < c1; tb += kRing * kBatch) {
 #pragma unroll
         for (int r = 0; r < kRing; ++r) {
-          const int sr = sb + r * kBatch;
-          if (t0 + hw + HW * sr < c1) {
+          const int tr = tb + r * kBatch;
+          if (tr < c1) {
             // every tile of the batch unconditionally (tiles past the range hold zero weights
             // and add nothing; their plane index is clamped into the array), so the scheduler
             // can read the next tile's planes while this one is reduced
@@ -320,7 +312,7 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
             for (int u = 0; u < kBatch; ++u) {
               {
                 const u32x4 wc = w[r][u];
-                const int pt = min(t0 + hw + HW * (sr + u) - c0, kChunk - 1);
+                const int pt = min(tr + u - c0, kChunk - 1);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                   const u32x4* X4 = reinterpret_cast<const u32x4*>(&pl[pt][m][0]);
@@ -338,29 +330,18 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
               }
             }
           }
-          load_batch(w[r], sr + kRing * kBatch);
+          load_batch(w[r], tr - t0 + kRing * kBatch);
         }
       }
     }
   }
+  if (!active) return;
+
   int acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m)
     acc[m] = A[m][0] + 2 * A[m][1] + 4 * A[m][2] + 8 * A[m][3] + 16 * A[m][4] + 32 * A[m][5] +
              64 * A[m][6] - 128 * A[m][7] + cn;
-  static_assert(HW == 1 || HW == 2, "one or two waves per band");
-  if constexpr (HW == 2) {   // the second wave of each band hands its sums to the first
-    __shared__ int red[kFW][MR][64];
-    if (hw == 1) {
-#pragma unroll
-      for (int m = 0; m < MR; ++m) red[wave - kFW][m][lane] = acc[m];
-    }
-    __syncthreads();
-    if (hw == 1) return;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] += red[wave][m][lane];
-  }
-  if (!active) return;
   const int64_t n = band * 64 + lane;
   const float b = beta[beta_len == 1 ? 0 : n];
 #pragma unroll
@@ -372,8 +353,6 @@ __global__ __launch_bounds__(64 * kFW * HW) void gemv_fused_kernel(
 }
 
 // Split plan of the fused kernel: workgroups own four bands each.
-
-constexpr int kFusedHW = 2;   // waves per band
 
 struct GemvFusedPlan { int64_t groups, nsplit, tps; };
 
@@ -445,11 +424,10 @@ hipError_t launch_gemv_fused(const uint16_t* x, int M, int64_t K, const void* wp
   const dim3 grid(static_cast<unsigned>(p.groups), static_cast<unsigned>(p.nsplit));
   const u32x4* W = static_cast<const u32x4*>(wpacked);
 #define BL_GEMVF_LAUNCH(MR_, GL_)                                                            \
-  hipLaunchKernelGGL((gemv_fused_kernel<MR_, GL_, kFusedHW>), grid, dim3(64 * kFW * kFusedHW), \
-                     0, s, x, K, W, beta, beta_len, N, y, ws_acc, ws_cnt,                     \
-                     static_cast<int>(p.tps))
-  // gamma loads unrolled per thread: K <= 512 kFW HW GL (row loads in registers); longer rows loop
-  const int64_t gl = (K / 8 + 64 * kFW * kFusedHW - 1) / (64 * kFW * kFusedHW);
+  hipLaunchKernelGGL((gemv_fused_kernel<MR_, GL_>), grid, dim3(64 * kFW), 0, s, x, K, W, beta, \
+                     beta_len, N, y, ws_acc, ws_cnt, static_cast<int>(p.tps))
+  // gamma loads unrolled per thread: K <= 512 kFW GL (row loads in registers); longer rows loop
+  const int64_t gl = (K / 8 + 64 * kFW - 1) / (64 * kFW);
   switch (M) {
     case 1:
       if (gl <= 2) BL_GEMVF_LAUNCH(1, 2);
