@@ -148,9 +148,12 @@ __global__ __launch_bounds__(256) void gemm_rb_kernel(
           const int64_t row = m0 + 16 * i + 4 * g + r;
           const int64_t col = n0 + 16 * j + u;
           if (row >= M) continue;
-          if (acc_out) acc_out[row * N + col] = acc[i][j][r];
-          if (y) y[row * N + col] = static_cast<float>(acc[i][j][r]) * (gamma[row] / 127.0f) *
-                                    beta[beta_len == 1 ? 0 : col];
+          // written once, not read back here: non-temporal stores
+          if (acc_out) __builtin_nontemporal_store(acc[i][j][r], &acc_out[row * N + col]);
+          if (y)
+            __builtin_nontemporal_store(static_cast<float>(acc[i][j][r]) * (gamma[row] / 127.0f) *
+                                            beta[beta_len == 1 ? 0 : col],
+                                        &y[row * N + col]);
         }
   } else {
 #pragma unroll

@@ -506,9 +506,11 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
         const int v = st[r * kStRow + lane] - (lane < 48 ? rsv : 0);   // fragments f < 3
         const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs_l), rr));
         const int64_t row = m0 + rr;
+        // outputs are written once and not read back here: non-temporal stores (measured on
+        // MI355X, 3B-shaped prefill at M = 512: the four products 1195 -> 1262 TOPS)
         if (active && row < a.M) {
-          if (a.acc_out) a.acc_out[row * a.N + col] = v;
-          if (a.y) a.y[row * a.N + col] = static_cast<float>(v) * gs * bcol;
+          if (a.acc_out) __builtin_nontemporal_store(v, &a.acc_out[row * a.N + col]);
+          if (a.y) __builtin_nontemporal_store(static_cast<float>(v) * gs * bcol, &a.y[row * a.N + col]);
         }
       }
       __syncthreads();
