@@ -314,7 +314,33 @@ def bench_prefill3b(torch, tw, synth, dev, steps, warmup):
     res["weights"] = "T2-MF64"
     pn = measure(gemm_pn)
     res["t2pn"] = {k: pn[k] for k in ("ms_per_pass", "ms_gemms_only", "tops_gemms", "frac_peak_gemms")}
+    res["library_int8"] = library_int8_gemms(torch, dev, items, M, steps, warmup)
     return res
+
+
+def library_int8_gemms(torch, dev, items, M, steps, warmup):
+    """Context for the prefill figure: the vendor BLAS int8 GEMM (torch._int_mm) on the same
+    shapes, with the weights as dense int8 codes (4x the packed bytes), int32 outputs and no
+    epilogue; the faster of the two weight layouts per shape. Not part of the path."""
+    per_shape, ms_total, ops = {}, 0.0, 0
+    for it in items:
+        N, K = it["N"], it["K"]
+        best = None
+        for layout in ("KxN column-major", "KxN row-major"):
+            if layout.endswith("column-major"):
+                b = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev).t()
+            else:
+                b = torch.randint(-1, 2, (K, N), dtype=torch.int8, device=dev)
+            t = timed(torch, lambda: torch._int_mm(it["q"], b), steps, warmup)
+            if best is None or t < best[0]:
+                best = (t, layout)
+            del b
+        per_shape[f"{M}x{N}x{K}"] = dict(ms=best[0], tops=2 * M * N * K / (best[0] / 1e3) / 1e12,
+                                         weights=best[1])
+        ms_total += best[0]
+        ops += 2 * M * N * K
+    return dict(op="torch._int_mm (vendor BLAS), int8 x int8 -> int32", per_shape=per_shape,
+                ms_gemms=ms_total, tops_gemms=ops / (ms_total / 1e3) / 1e12)
 
 
 def bench_decode7b_stack(torch, tw, sgpu, synth, dev, steps, warmup):

@@ -108,6 +108,16 @@ __device__ __forceinline__ uint32_t sign_pair_bits(uint32_t word) {
   return (word << (15 - 4 * S - Q)) & 0x80008000u;
 }
 
+// The same shift for two words held in adjacent registers (hi:lo), as one v_lshlrev_b64 (the
+// compiler turns a 64-bit shift by a constant into two 32-bit operations). The shift is at
+// most 15, so bits 15 and 31 of the high word still come from the high word alone.
+template <int S, int Q>
+__device__ __forceinline__ uint64_t sign_pair_shift64(uint64_t words) {
+  uint64_t r;
+  asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "I"(15 - 4 * S - Q), "v"(words));
+  return r;
+}
+
 template <bool RES, int S>
 __device__ __forceinline__ void sign_slice(const SignTile<RES>& T, sm_f32x4 (&acc)[4],
                                            sm_f32x4 (&p)[4], sm_f32x4 (&r)[4], uint32_t one) {
@@ -285,8 +295,9 @@ __host__ __device__ constexpr int st_max_tiles(int64_t M) {
   return static_cast<int>(kStLdsBytes / ((M + 1) * 256));
 }
 constexpr int kStMaxPerWave = (st_max_tiles(1) + kStWaves - 1) / kStWaves;
-// PW: tiles per wave the kernel is built for (4 or kStMaxPerWave): every one of them is
-// loaded (clamped into the range), so short ranges take the small build. XG (5..16 rows of x):
+// PW: tiles per wave the kernel is built for (4, 8 or kStMaxPerWave): every one of them is
+// loaded (clamped into the range), so short ranges take a smaller build (measured on MI355X,
+// 28672 x 8192 at M = 1, 64 tiles per range: 17.0 us built for 12 tiles per wave, 16.3 for 8). XG (5..16 rows of x):
 // x is not staged but loaded per tile into registers with the sign words (lanes of rows past
 // M load row M - 1), only g goes through LDS; built for PW = 4.
 template <bool RES, int NF, int PW, bool XG>
@@ -403,7 +414,26 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
         sm_f16x8 av;
         if constexpr (XG) av = __builtin_bit_cast(sm_f16x8, xv[j][S]);
         else av = *reinterpret_cast<const sm_f16x8*>(xrow + tl * 128 + 32 * S);
-        if constexpr (!RES) {
+        if constexpr (!RES && NF == 4) {
+          // one 64-bit shift aligns the words of fragments 2p and 2p + 1 (one sign record,
+          // adjacent registers): 12 VALU operations per two MFMAs instead of 16, which are the
+          // bound at M = 1 (measured on MI355X, 28672 x 8192 at M = 1: 16.3 -> 15.55 us)
+          const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
+#pragma unroll
+          for (int fp = 0; fp < 2; ++fp) {
+            const uint64_t pw = (static_cast<uint64_t>(w0[j][2 * fp + 1]) << 32) | w0[j][2 * fp];
+            const uint64_t sh[4] = {sign_pair_shift64<S, 0>(pw), sign_pair_shift64<S, 1>(pw),
+                                    sign_pair_shift64<S, 2>(pw), sign_pair_shift64<S, 3>(pw)};
+            sm_u32x4 b0, b1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              b0[q] = gv[q] ^ (static_cast<uint32_t>(sh[q]) & 0x80008000u);
+              b1[q] = gv[q] ^ (static_cast<uint32_t>(sh[q] >> 32) & 0x80008000u);
+            }
+            acc[2 * fp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b0), acc[2 * fp], 0, 0, 0);
+            acc[2 * fp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b1), acc[2 * fp + 1], 0, 0, 0);
+          }
+        } else if constexpr (!RES) {
           const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
@@ -562,13 +592,16 @@ inline hipError_t launch_sign_mfma(const SignMfmaArgs& args, hipStream_t s) {
                   static_cast<unsigned>(p.nsplit));
   const dim3 block(64 * kStWaves);
   const bool small = p.tps <= 4 * kStWaves;   // at most four tiles per wave
+  const bool mid = p.tps <= 8 * kStWaves;     // at most eight
   if (p.kernel == 1) {
     if (p.xg) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4, true>), grid, block, 0, s, a);
     else if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 4, false>), grid, block, 0, s, a);
+    else if (mid) hipLaunchKernelGGL((sign_staged_kernel<RES, 1, 8, false>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((sign_staged_kernel<RES, 1, kStMaxPerWave, false>), grid, block, 0, s, a);
   } else if constexpr (!RES) {
     if (p.kernel == 4) {
       if (small) hipLaunchKernelGGL((sign_staged_kernel<RES, 4, 4, false>), grid, block, 0, s, a);
+      else if (mid) hipLaunchKernelGGL((sign_staged_kernel<RES, 4, 8, false>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((sign_staged_kernel<RES, 4, kStMaxPerWave, false>), grid, block, 0, s, a);
     } else {
       hipLaunchKernelGGL(sign_mfma_kernel<RES>, grid, dim3(256), 0, s, a);

@@ -372,12 +372,13 @@ def _onebit_inputs(M, N, K, seed=0):
                                    (4, 256, 640), (33, 192, 512), (17, 1024, 8192),
                                    (1, 512, 8192), (1, 16384, 256), (2, 16384, 384),
                                    (4, 16384, 5120), (1, 2048, 12288), (8, 1024, 8192),
-                                   (12, 16384, 256)])
+                                   (12, 16384, 256), (1, 16384, 4224), (3, 16384, 6144)])
 def test_onebit(M, N, K):
     """Covers the three workgroup mappings: at M <= 4 one 16-column fragment per workgroup
     (few bands; (1, 512, 8192) also splits K) or one band per workgroup with x and g staged
     in LDS (N = 16384: 256 bands; (4, 16384, 5120) splits K because its range would not fit
-    LDS), and the band kernel above M = 4."""
+    LDS; K = 4224 and 6144 take the build for 33..64 tiles per range), and the band kernel
+    above M = 4."""
     say("onebit", M, N, K)
     x, g, h, W = _onebit_inputs(M, N, K)
     S = np.where(W < 0, -1, 1).astype(np.int8)
