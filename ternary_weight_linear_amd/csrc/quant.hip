@@ -144,7 +144,9 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
 #pragma unroll
   for (int n = 0; n < NV; ++n) {
     const int64_t i = threadIdx.x + BLOCK * n;
-    if (i >= K8) break;
+    // a guarded body, not a break: with a break the compiler left the loop rolled for NV = 16
+    // and indexed v[] in scratch memory (272 bytes per lane)
+    if (i >= K8) continue;
     const uint32_t w[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
     float a[8], ge[8], rge[8];
     bool ze[8];
@@ -180,14 +182,19 @@ __global__ __launch_bounds__(BLOCK) void quant_act_regs_kernel(const uint16_t* _
 hipError_t launch_quant_act(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* gamma,
                             int32_t* rowsum, uint32_t* planes, hipStream_t s) {
   if (!planes) {
-    // one workgroup per row, every input of the row in registers
+    // one workgroup per row, every input of the row in registers: the smallest build whose
+    // BLOCK * NV 16-byte loads cover the row (the loads past it repeat its last piece)
     const int64_t K8 = K / 8;
+    const dim3 grid(static_cast<unsigned>(M));
     if (M <= 64) {
-      if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<1024, 1>), dim3(static_cast<unsigned>(M)), dim3(1024), 0, s, x, K, q, gamma, rowsum);
-      else hipLaunchKernelGGL((quant_act_regs_kernel<1024, 4>), dim3(static_cast<unsigned>(M)), dim3(1024), 0, s, x, K, q, gamma, rowsum);
+      if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<1024, 1>), grid, dim3(1024), 0, s, x, K, q, gamma, rowsum);
+      else if (K8 <= 2048) hipLaunchKernelGGL((quant_act_regs_kernel<1024, 2>), grid, dim3(1024), 0, s, x, K, q, gamma, rowsum);
+      else hipLaunchKernelGGL((quant_act_regs_kernel<1024, 4>), grid, dim3(1024), 0, s, x, K, q, gamma, rowsum);
     } else {
-      if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<256, 4>), dim3(static_cast<unsigned>(M)), dim3(256), 0, s, x, K, q, gamma, rowsum);
-      else hipLaunchKernelGGL((quant_act_regs_kernel<256, 16>), dim3(static_cast<unsigned>(M)), dim3(256), 0, s, x, K, q, gamma, rowsum);
+      if (K8 <= 512) hipLaunchKernelGGL((quant_act_regs_kernel<256, 2>), grid, dim3(256), 0, s, x, K, q, gamma, rowsum);
+      else if (K8 <= 1024) hipLaunchKernelGGL((quant_act_regs_kernel<256, 4>), grid, dim3(256), 0, s, x, K, q, gamma, rowsum);
+      else if (K8 <= 2048) hipLaunchKernelGGL((quant_act_regs_kernel<256, 8>), grid, dim3(256), 0, s, x, K, q, gamma, rowsum);
+      else hipLaunchKernelGGL((quant_act_regs_kernel<256, 16>), grid, dim3(256), 0, s, x, K, q, gamma, rowsum);
     }
     return hipGetLastError();
   }
