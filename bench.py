@@ -234,6 +234,50 @@ def graphed(torch, fn):
     return g.replay, g
 
 
+def read_floor_pass(torch, dev, layers, steps, warmup):
+    """The decode pass with every GEMV launch replaced by a streaming read of the same packed
+    weight buffer (stream_read_slices_kernel: one contiguous slice per workgroup, non-temporal
+    loads), launched in the same order and replayed from a HIP graph like the timed pass: what
+    320 dependent launches over these sizes cost with no arithmetic at all. The grid is the
+    fastest of a few per buffer size."""
+    import ctypes
+    lib = ctypes.CDLL(CEIL_LIB)
+    P = ctypes.c_void_p
+    lib.bl_ceil_stream_read_slices.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    out = torch.zeros(4096, dtype=torch.int32, device=dev)
+    bufs = [(buf, buf.numel()) for lg in layers for (_, buf, _, _) in lg]
+    grids = {}
+    for nb in sorted({n for _, n in bufs}):
+        cands = [g for g in (128, 160, 256, 320, 448, 512, 640, 896, 1024, 1792, 2048)
+                 if nb % (g * 32768) == 0]
+        same = [b for b, n in bufs if n == nb]
+        best = None
+        for g in cands:
+            def sweep(g=g):
+                st = P(torch.cuda.current_stream().cuda_stream)
+                for b in same:
+                    assert lib.bl_ceil_stream_read_slices(P(b.data_ptr()), nb, P(out.data_ptr()), g, st) == 0
+            run, keep = graphed(torch, sweep)
+            t = timed(torch, run, 3, 1) / len(same)
+            del run, keep
+            if best is None or t < best[0]:
+                best = (t, g)
+        grids[nb] = best
+
+    def full_pass():
+        st = P(torch.cuda.current_stream().cuda_stream)
+        for b, nb in bufs:
+            assert lib.bl_ceil_stream_read_slices(P(b.data_ptr()), nb, P(out.data_ptr()), grids[nb][1], st) == 0
+
+    run, keep = graphed(torch, full_pass)
+    ms = timed(torch, run, steps, warmup)
+    del run, keep
+    return {"ms_per_pass": ms, "launches_per_pass": len(bufs),
+            "us_per_launch_by_bytes": {str(nb): round(t * 1e3, 3) for nb, (t, g) in grids.items()},
+            "grid_by_bytes": {str(nb): g for nb, (t, g) in grids.items()},
+            "kernel": "stream_read_slices_kernel (ceilings.hip)"}
+
+
 def bench_decode70b(torch, tw, synth, dev, layers, M, steps, warmup, use_graph=True):
     items, full_pass, algo, wbytes, launches = decode_pass(torch, tw, synth, dev, layers, M)
     ms_eager = timed(torch, full_pass, max(1, steps // 4), 1 if warmup else 0)
@@ -729,6 +773,8 @@ def main():
             layers_mf = repack_stack_mf(torch, tw, dev, layers)
             res = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, M, args.steps, args.warmup,
                                      use_graph=not args.no_graph)
+        elif args.only == "read_floor":
+            res = read_floor_pass(torch, dev, layers, args.steps, args.warmup)
         elif args.only.startswith("stack_m"):
             M = int(args.only.split("_m")[1])
             res = bench_decode70b_stack(torch, tw, synth, dev, layers, M, args.steps, args.warmup)
@@ -739,6 +785,10 @@ def main():
     main_res = bench_decode70b(torch, tw, synth, dev, layers, 1, args.steps, args.warmup,
                                use_graph=not args.no_graph)
     log("decode70b M=1:", json.dumps(main_res))
+    read_floor = None
+    if not args.skip_extra:
+        read_floor = read_floor_pass(torch, dev, layers, args.steps, args.warmup)
+        log("the same pass as streaming reads only:", json.dumps(read_floor))
     if not args.skip_extra:
         layers_mf = repack_stack_mf(torch, tw, dev, layers)
         r = bench_decode70b_mf(torch, tw, synth, dev, layers_mf, 1, args.steps, args.warmup)
@@ -824,9 +874,14 @@ def main():
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": round(per_launch_bytes, 1),
                      "frac_measured_peak": (round(achieved / ceilings["hbm_read_gbs"], 4)
-                                            if ceilings else None)},
+                                            if ceilings else None),
+                     # the pass against the same launches doing nothing but read their weights
+                     "launch_read_floor_ms": round(read_floor["ms_per_pass"], 4) if read_floor else None,
+                     "frac_launch_read_floor": (round(read_floor["ms_per_pass"] / ms, 4)
+                                                if read_floor else None)},
         "roofline_gemm": roofline_gemm,
         "measured_ceilings": ceilings,
+        "launch_read_floor": read_floor,
         "extra": extra,
     }
     if not args.skip_cpu:
