@@ -236,46 +236,52 @@ def graphed(torch, fn):
 
 def read_floor_pass(torch, dev, layers, steps, warmup):
     """The decode pass with every GEMV launch replaced by a streaming read of the same packed
-    weight buffer (stream_read_slices_kernel: one contiguous slice per workgroup, non-temporal
-    loads), launched in the same order and replayed from a HIP graph like the timed pass: what
-    320 dependent launches over these sizes cost with no arithmetic at all. The grid is the
-    fastest of a few per buffer size."""
+    weight buffer (one contiguous slice per workgroup with non-temporal loads, or grid-strided
+    reads), launched in the same order and replayed from a HIP graph like the timed pass: what
+    the pass's dependent launches over these sizes cost with no arithmetic at all. The read
+    and its grid are the fastest of a few per buffer size."""
     import ctypes
     lib = ctypes.CDLL(CEIL_LIB)
     P = ctypes.c_void_p
-    lib.bl_ceil_stream_read_slices.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
+    for fn in (lib.bl_ceil_stream_read, lib.bl_ceil_stream_read_slices):
+        fn.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     out = torch.zeros(4096, dtype=torch.int32, device=dev)
     bufs = [(buf, buf.numel()) for lg in layers for (_, buf, _, _) in lg]
-    grids = {}
+    kinds = {"slices": lib.bl_ceil_stream_read_slices, "strided": lib.bl_ceil_stream_read}
+    best_by = {}
     for nb in sorted({n for _, n in bufs}):
-        cands = [g for g in (128, 160, 256, 320, 448, 512, 640, 896, 1024, 1792, 2048)
+        # slices where the size divides into whole 32 KiB pieces per workgroup, grid-strided
+        # reads (any size) otherwise or where faster
+        cands = [("slices", g) for g in (128, 160, 256, 320, 448, 512, 640, 896, 1024, 1792, 2048)
                  if nb % (g * 32768) == 0]
+        cands += [("strided", g) for g in (512, 1024, 2048, 4096)]
         same = [b for b, n in bufs if n == nb]
         best = None
-        for g in cands:
-            def sweep(g=g):
+        for kind, g in cands:
+            def sweep(kind=kind, g=g):
                 st = P(torch.cuda.current_stream().cuda_stream)
                 for b in same:
-                    assert lib.bl_ceil_stream_read_slices(P(b.data_ptr()), nb, P(out.data_ptr()), g, st) == 0
+                    assert kinds[kind](P(b.data_ptr()), nb, P(out.data_ptr()), g, st) == 0
             run, keep = graphed(torch, sweep)
             t = timed(torch, run, 3, 1) / len(same)
             del run, keep
             if best is None or t < best[0]:
-                best = (t, g)
-        grids[nb] = best
+                best = (t, kind, g)
+        best_by[nb] = best
 
     def full_pass():
         st = P(torch.cuda.current_stream().cuda_stream)
         for b, nb in bufs:
-            assert lib.bl_ceil_stream_read_slices(P(b.data_ptr()), nb, P(out.data_ptr()), grids[nb][1], st) == 0
+            _, kind, g = best_by[nb]
+            assert kinds[kind](P(b.data_ptr()), nb, P(out.data_ptr()), g, st) == 0
 
     run, keep = graphed(torch, full_pass)
     ms = timed(torch, run, steps, warmup)
     del run, keep
     return {"ms_per_pass": ms, "launches_per_pass": len(bufs),
-            "us_per_launch_by_bytes": {str(nb): round(t * 1e3, 3) for nb, (t, g) in grids.items()},
-            "grid_by_bytes": {str(nb): g for nb, (t, g) in grids.items()},
-            "kernel": "stream_read_slices_kernel (ceilings.hip)"}
+            "us_per_launch_by_bytes": {str(nb): round(t * 1e3, 3) for nb, (t, k, g) in best_by.items()},
+            "read_by_bytes": {str(nb): f"{k}, {g} workgroups" for nb, (t, k, g) in best_by.items()},
+            "kernel": "stream_read_slices_kernel / stream_read_kernel (ceilings.hip)"}
 
 
 def bench_decode70b(torch, tw, synth, dev, layers, M, steps, warmup, use_graph=True):
@@ -400,6 +406,10 @@ def bench_decode7b_stack(torch, tw, sgpu, synth, dev, steps, warmup):
     out["weights"] = "T2-MF64"
     r = bench_decode70b(torch, tw, synth, dev, layers, 1, steps, warmup)
     out["t2pn_gemv"] = {k: r[k] for k in ("ms_per_pass", "tokens_per_s", "gbs")}
+    # the same 128 launches reading their weights and nothing else
+    rf = read_floor_pass(torch, dev, layers, steps, warmup)
+    out["launch_read_floor_ms"] = rf["ms_per_pass"]
+    out["frac_launch_read_floor"] = rf["ms_per_pass"] / out["ms_per_pass"]
     del layers
     return out
 
