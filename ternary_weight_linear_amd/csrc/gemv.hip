@@ -375,9 +375,6 @@ GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
 
 struct GemvPlan { int64_t nsplit, tps; };
 
-// Workgroups the split-K plan aims for (0: by shape). Only tuning harnesses that compile
-// this file directly change it.
-
 GemvPlan plan_gemv(int M, int64_t N, int64_t K) {
   const int64_t bands = N / 64;
   const int64_t KT = K / 64;
