@@ -544,10 +544,8 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
 // workgroup, 4 = staged kernel with one band per workgroup; xg: x loaded per tile (5..16 rows).
 struct SignPlan { int64_t cols, mtiles, nsplit, tps; int kernel; bool xg; };
 
-// Workgroups to aim for. Tuning harnesses that compile the sources directly may set it
-// (0 = the default); the workspace is sized for the default.
+// Workgroups to aim for (one per CU); the workspace is sized with the same plan.
 constexpr int64_t kSignWgTarget = 256;
-inline int64_t sign_wg_target() { return kSignWgTarget; }
 
 // Decode-sized batches (M <= 16) take the staged kernel: one fragment per workgroup where
 // the bands leave the chip short of `target` workgroups; at M <= 4 (x staged in LDS) one band
@@ -584,7 +582,7 @@ inline SignPlan plan_sign_mfma(int64_t M, int64_t N, int64_t K, int64_t target, 
 
 template <bool RES>
 inline hipError_t launch_sign_mfma(const SignMfmaArgs& args, hipStream_t s) {
-  const SignPlan p = plan_sign_mfma(args.M, args.N, args.K, sign_wg_target(), RES);
+  const SignPlan p = plan_sign_mfma(args.M, args.N, args.K, kSignWgTarget, RES);
   SignMfmaArgs a = args;
   a.tiles_per_split = static_cast<int>(p.tps);
   a.one = 0x3C003C00u;
