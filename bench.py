@@ -236,23 +236,28 @@ def graphed(torch, fn):
 
 def read_floor_pass(torch, dev, layers, steps, warmup):
     """The decode pass with every GEMV launch replaced by a streaming read of the same packed
-    weight buffer (one contiguous slice per workgroup with non-temporal loads, or grid-strided
-    reads), launched in the same order and replayed from a HIP graph like the timed pass: what
-    the pass's dependent launches over these sizes cost with no arithmetic at all. The read
-    and its grid are the fastest of a few per buffer size."""
+    weight buffer, launched in the same order and replayed from a HIP graph like the timed
+    pass: what the pass's dependent launches over these sizes cost with no arithmetic."""
+    return read_floor(torch, dev, [buf for lg in layers for (_, buf, _, _) in lg], steps, warmup)
+
+
+def read_floor(torch, dev, buffers, steps, warmup):
+    """One streaming read per buffer (one contiguous slice per workgroup with non-temporal
+    loads, or grid-strided reads), in order, replayed from a HIP graph. The read and its grid
+    are the fastest of a few per buffer size."""
     import ctypes
     lib = ctypes.CDLL(CEIL_LIB)
     P = ctypes.c_void_p
     for fn in (lib.bl_ceil_stream_read, lib.bl_ceil_stream_read_slices):
         fn.argtypes = [P, ctypes.c_int64, P, ctypes.c_int, P]
     out = torch.zeros(4096, dtype=torch.int32, device=dev)
-    bufs = [(buf, buf.numel()) for lg in layers for (_, buf, _, _) in lg]
+    bufs = [(buf, buf.numel()) for buf in buffers]
     kinds = {"slices": lib.bl_ceil_stream_read_slices, "strided": lib.bl_ceil_stream_read}
     best_by = {}
     for nb in sorted({n for _, n in bufs}):
         # slices where the size divides into whole 32 KiB pieces per workgroup, grid-strided
         # reads (any size) otherwise or where faster
-        cands = [("slices", g) for g in (128, 160, 256, 320, 448, 512, 640, 896, 1024, 1792, 2048)
+        cands = [("slices", g) for g in (32, 64, 128, 160, 256, 320, 448, 512, 640, 896, 1024, 1792, 2048)
                  if nb % (g * 32768) == 0]
         cands += [("strided", g) for g in (512, 1024, 2048, 4096)]
         same = [b for b, n in bufs if n == nb]
@@ -491,6 +496,8 @@ def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
         out[f"M{M}"] = dict(us_per_layer=ms * 1e3 / pool, us_per_layer_eager=ms_eager * 1e3 / pool,
                             gbs_signs=pool * N * K / 8 / (ms / 1e3) / 1e9,
                             stored_bits_per_layer=8 * spool[0].numel() + 16 * (N + K), graph=True)
+    # the same launches reading their sign matrices and nothing else
+    out["launch_read_floor_us_per_layer"] = read_floor(torch, dev, spool, max(2, steps // 4), 1)["ms_per_pass"] * 1e3 / pool
     # a 70B-sized matrix (28672 x 8192, 29 MiB of signs) at M = 1, pool of 16
     N2, K2, pool2 = 28672, 8192, 16
     W = torch.from_numpy(synth.normal_fp32((N2, K2), 0, 2, 5, 0)).to(dev)
@@ -513,7 +520,8 @@ def bench_onebit(torch, tw, synth, dev, steps, warmup, pool=256):
     run, keep = graphed(torch, sweep2)
     ms = timed(torch, run, max(2, steps // 4), 1)
     out["28672x8192_M1"] = dict(us_per_layer=ms * 1e3 / pool2,
-                                gbs_signs=pool2 * N2 * K2 / 8 / (ms / 1e3) / 1e9, graph=True)
+                                gbs_signs=pool2 * N2 * K2 / 8 / (ms / 1e3) / 1e9, graph=True,
+                                launch_read_floor_us=read_floor(torch, dev, spool2, max(2, steps // 4), 1)["ms_per_pass"] * 1e3 / pool2)
     return out
 
 
