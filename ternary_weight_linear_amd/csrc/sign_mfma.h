@@ -400,6 +400,18 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
   sm_f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = sm_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // The LDS operands of the next slice (x unless it comes from registers, g for OneBit) are
+  // read while the current slice's products run; read just before use, every slice waited
+  // for its LDS reads in front of its MFMAs. Past the wave's last tile the reads stay inside
+  // the staged range (their values are not used).
+  sm_f16x8 an{};
+  sm_u32x4 gn{};
+  auto read_next = [&](int tile, int sl) __attribute__((always_inline)) {
+    const int t = min(tile, nt - 1);
+    if constexpr (!XG) an = *reinterpret_cast<const sm_f16x8*>(xrow + t * 128 + 32 * sl);
+    if constexpr (!RES) gn = *reinterpret_cast<const sm_u32x4*>(grow + t * 128 + 32 * sl);
+  };
+  read_next(wave, 0);
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
     if (j < n) {
@@ -413,12 +425,14 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
         constexpr int S = decltype(sc)::value;
         sm_f16x8 av;
         if constexpr (XG) av = __builtin_bit_cast(sm_f16x8, xv[j][S]);
-        else av = *reinterpret_cast<const sm_f16x8*>(xrow + tl * 128 + 32 * S);
+        else av = an;
+        const sm_u32x4 gv = gn;
+        if constexpr (S < 3) read_next(tl, S + 1);
+        else read_next(tl + kStWaves, 0);
         if constexpr (!RES && NF == 4) {
           // one 64-bit shift aligns the words of fragments 2p and 2p + 1 (one sign record,
           // adjacent registers): 12 VALU operations per two MFMAs instead of 16, which are the
           // bound at M = 1 (measured on MI355X, 28672 x 8192 at M = 1: 16.3 -> 15.55 us)
-          const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
 #pragma unroll
           for (int fp = 0; fp < 2; ++fp) {
             const uint64_t pw = (static_cast<uint64_t>(w0[j][2 * fp + 1]) << 32) | w0[j][2 * fp];
@@ -434,7 +448,6 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
             acc[2 * fp + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(sm_f16x8, b1), acc[2 * fp + 1], 0, 0, 0);
           }
         } else if constexpr (!RES) {
-          const sm_u32x4 gv = *reinterpret_cast<const sm_u32x4*>(grow + tl * 128 + 32 * S);
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             sm_u32x4 b;
