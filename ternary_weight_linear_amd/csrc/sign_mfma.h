@@ -297,9 +297,9 @@ __host__ __device__ constexpr int st_max_tiles(int64_t M) {
 constexpr int kStMaxPerWave = (st_max_tiles(1) + kStWaves - 1) / kStWaves;
 // PW: tiles per wave the kernel is built for (4, 8 or kStMaxPerWave): every one of them is
 // loaded (clamped into the range), so short ranges take a smaller build (measured on MI355X,
-// 28672 x 8192 at M = 1, 64 tiles per range: 17.0 us built for 12 tiles per wave, 16.3 for 8). XG (5..16 rows of x):
-// x is not staged but loaded per tile into registers with the sign words (lanes of rows past
-// M load row M - 1), only g goes through LDS; built for PW = 4.
+// 28672 x 8192 at M = 1, 64 tiles per range: 17.0 us built for 12 tiles per wave, 16.3 for
+// 8). XG (5..16 rows of x): x is not staged but loaded per tile into registers with the sign
+// words (lanes of rows past M load row M - 1), only g goes through LDS; built for PW = 4.
 template <bool RES, int NF, int PW, bool XG>
 __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMfmaArgs a) {
   constexpr int kPad = 68;

@@ -115,8 +115,12 @@ def _quant_case(x):
                                   oracle.act_planes(rq))
 
 
+# Rows of up to 64 take 1024-thread workgroups with 1, 2 or 4 loads per thread (K up to 8192,
+# 16384, 32768), more rows 256-thread workgroups with 2, 4, 8 or 16 (K up to 4096, 8192, 16384,
+# 32768): each build at its largest K and just past it, and the 3B-shaped prefill inputs.
 @pytest.mark.parametrize("M,K", [(1, 64), (8, 512), (3, 640), (1, 8192), (4, 28672), (512, 3200),
-                                 (65, 8192), (70, 28672), (64, 8256)])
+                                 (65, 8192), (70, 28672), (64, 8256), (2, 16384), (3, 16448),
+                                 (66, 4096), (66, 4160), (100, 16384), (512, 8640)])
 def test_quant_act(M, K):
     say("quant_act", M, K)
     x = synth.normal_fp16((M, K), 0, 2, M, K)
