@@ -855,7 +855,7 @@ def main():
     roofline_gemm = None
     if "prefill3b_m512" in extra:
         pf = extra["prefill3b_m512"]
-        roofline_gemm = {"bound": "mfma", "kernel": "tern_mfq_kernel<FM> (staged-q int8 MFMA, T2-MF64)",
+        roofline_gemm = {"bound": "mfma", "kernel": "tern_mfq_kernel<FM, 4> (staged-q int8 MFMA, T2-MF64, four bands per workgroup)",
                          "workload": "3B-shaped prefill, M=512: q|k|v 512x9600x3200, o 512x3200x3200, "
                                      "gate|up 512x17280x3200, down 512x3200x8640",
                          "achieved": round(pf["tops_gemms"], 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",

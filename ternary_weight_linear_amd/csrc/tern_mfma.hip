@@ -352,19 +352,30 @@ constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elemen
 
 // 48-row tiles are held to 168 VGPRs (three workgroups per CU instead of two): a 3B-shaped
 // prefill then runs its work items in one round instead of one and a half.
-template <int FM>
+// BW = 2: a work item is two bands, and each band's K range is split in two halves taken by
+// two waves (waves 2 and 3 take the second halves, with their own q chunks in LDS); the
+// halves' sums meet in LDS. Twice the work items of BW = 4 without split words, for row
+// tiles that would leave CUs idle.
+template <int FM, int BW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 3 ? 3 : 1)))
 void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   constexpr int kRows = 16 * FM;
   constexpr int R = FM == 3 ? kQRing3 : kQRing;
-  constexpr int kSegs = kRows * kQC * 4 / 256;   // 16-byte pieces of q per thread per chunk
-  static_assert(kSegs >= 1 && (kRows * kQC * 4) % 256 == 0, "q chunk copy");
+  constexpr int KS = 4 / BW;                       // K halves per band
+  constexpr int kHT = 256 / KS;                    // threads per half
+  constexpr int kSegs = kRows * kQC * 4 / kHT;     // 16-byte pieces of q per thread per chunk
+  static_assert(BW == 4 || BW == 2, "four bands, or two bands in two halves");
+  static_assert(kSegs >= 1 && (kRows * kQC * 4) % kHT == 0, "q chunk copy");
   constexpr int kQBuf = kRows * kQPitch;           // one staged chunk of q
-  constexpr int kLds = 2 * kQBuf > 4 * 16 * kStRow * 4 ? 2 * kQBuf : 4 * 16 * kStRow * 4;
+  constexpr int kStBytes = 4 * 16 * kStRow * 4;    // result rows of the epilogue
+  constexpr int kRedBytes = KS > 1 ? BW * FM * 16 * 64 * 4 : 0;   // second halves' sums
+  constexpr int kLds = 2 * KS * kQBuf > kStBytes + kRedBytes ? 2 * KS * kQBuf : kStBytes + kRedBytes;
   __shared__ __attribute__((aligned(16))) int8_t lds[kLds];   // q chunks, then results
-  auto qs = [&](int buf) __attribute__((always_inline)) { return lds + buf * kQBuf; };
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % BW);   // band within the item
+  const int half = KS > 1 ? __builtin_amdgcn_readfirstlane(tid / kHT) : 0;
+  const int htid = tid % kHT;                                        // thread within the half
+  auto qs = [&](int buf) __attribute__((always_inline)) { return lds + (half * 2 + buf) * kQBuf; };
   const int g = lane >> 4, u = lane & 15;
   const int64_t bands = a.N / 64;
   const int KT = static_cast<int>(a.K / 64);
@@ -372,7 +383,7 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   // runs on XCD i % 8); each XCD takes a contiguous range of work items, ordered split,
   // band group, row group (fastest), so the row groups of a band group run side by side on
   // one XCD and read its weights through that XCD's L2 once instead of once per row group.
-  const int groups = static_cast<int>((bands + 3) / 4);
+  const int groups = static_cast<int>((bands + BW - 1) / BW);
   const int mgroups = static_cast<int>((a.M + kRows - 1) / kRows);
   const int nsplit = (KT + a.tiles_per_split - 1) / a.tiles_per_split;
   const int nwork = groups * mgroups * nsplit;
@@ -382,11 +393,16 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   const int mg = wk % mgroups;
   const int grp = (wk / mgroups) % groups;
   const int split = wk / (mgroups * groups);
-  const int64_t band = static_cast<int64_t>(grp) * 4 + wave;
+  const int64_t band = static_cast<int64_t>(grp) * BW + wave;
   const bool active = band < bands;
   const int64_t m0 = static_cast<int64_t>(mg) * kRows;
-  const int t0 = split * a.tiles_per_split;
-  const int t1 = min(KT, t0 + a.tiles_per_split);
+  const int s0 = split * a.tiles_per_split;
+  const int s1 = min(KT, s0 + a.tiles_per_split);
+  // this half's chunks: [half * nchh, (half + 1) * nchh) of the item's; both halves run nchh
+  // steps in lockstep (a half with fewer chunks multiplies zero weights)
+  const int nchh = ((s1 - s0 + kQC - 1) / kQC + KS - 1) / KS;
+  const int t0 = min(s1, s0 + half * nchh * kQC);
+  const int t1 = min(s1, t0 + nchh * kQC);
   const int nch = (t1 - t0 + kQC - 1) / kQC;
 
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -400,14 +416,14 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
                                              wr, (chunk * kQC + t) * 1024 + lane * 16, 0, 0));
     __builtin_amdgcn_sched_barrier(0);   // keep each batch where it is issued
   };
-  // q piece s = tid + 256 i of a chunk: row s / (4 kQC), tile (s / 4) % kQC, 16 bytes s % 4.
+  // q piece s = htid + kHT i of a chunk: row s / (4 kQC), tile (s / 4) % kQC, 16 bytes s % 4.
   // Rows past M and tiles past K are clamped into q (their products are never stored or
   // meet zero weights).
   u32x4 qr[R][kSegs];
   auto load_q = [&](u32x4 (&dst)[kSegs], int chunk) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
-      const int sg = tid + 256 * i;
+      const int sg = htid + kHT * i;
       const int64_t row = min<int64_t>(m0 + sg / (4 * kQC), a.M - 1);
       const int tile = min(t0 + chunk * kQC + (sg / 4) % kQC, KT - 1);
       dst[i] = *reinterpret_cast<const u32x4*>(a.q + row * a.K + tile * 64 + (sg % 4) * 16);
@@ -416,7 +432,7 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   auto store_q = [&](const u32x4 (&src)[kSegs], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < kSegs; ++i) {
-      const int sg = tid + 256 * i;
+      const int sg = htid + kHT * i;
       *reinterpret_cast<u32x4*>(qs(buf) + (sg / (4 * kQC)) * kQPitch + ((sg / 4) % kQC) * 64 +
                                 (sg % 4) * 16) = src[i];
     }
@@ -468,7 +484,7 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   __syncthreads();
   // chunk c: weights and q registers in ring slot c % R, q in LDS buffer c % 2. Step c
   // reduces chunk c, reloads its slot with chunk c + R, stores chunk c + 1's q, one barrier.
-  for (int c0 = 0; c0 < nch; c0 += R) {
+  for (int c0 = 0; c0 < nchh; c0 += R) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int c = c0 + r;
@@ -477,6 +493,28 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
       load_w(w[r], c + R);
       store_q(qr[(r + 1) % R], (c + 1) & 1);
       __syncthreads();
+    }
+  }
+  if constexpr (KS > 1) {
+    // the second halves' sums join the first halves', lane for lane
+    __syncthreads();                        // every wave is done with the q chunks
+    int* red = reinterpret_cast<int*>(lds + kStBytes) + wave * FM * 16 * 64;
+    if (half) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((fm * 4 + f) * 4 + i) * 64 + lane] = acc[fm][f][i];
+    }
+    __syncthreads();
+    if (!half) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[fm][f][i] += red[((fm * 4 + f) * 4 + i) * 64 + lane];
     }
   }
   // Without a K split the integers leave through LDS as whole rows: each wave stages its
@@ -495,9 +533,11 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
     const float gs_l = a.y != nullptr ? a.gamma[rl] / 127.0f : 0.0f;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
+      if (!half) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k)   // output k: row 4g + k % 4, column 16 (k / 4) + u
-        st[(4 * g + k % 4) * kStRow + 16 * (k / 4) + u] = acc[fm][k / 4][k % 4] >> (2 * (k / 4));
+        for (int k = 0; k < 16; ++k)   // output k: row 4g + k % 4, column 16 (k / 4) + u
+          st[(4 * g + k % 4) * kStRow + 16 * (k / 4) + u] = acc[fm][k / 4][k % 4] >> (2 * (k / 4));
+      }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -508,7 +548,7 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
         const int64_t row = m0 + rr;
         // outputs are written once and not read back here: non-temporal stores (measured on
         // MI355X, 3B-shaped prefill at M = 512: the four products 1195 -> 1262 TOPS)
-        if (active && row < a.M) {
+        if (!half && active && row < a.M) {
           if (a.acc_out) __builtin_nontemporal_store(v, &a.acc_out[row * a.N + col]);
           if (a.y) __builtin_nontemporal_store(static_cast<float>(v) * gs * bcol, &a.y[row * a.N + col]);
         }
@@ -517,7 +557,7 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
     }
     return;
   }
-  if (!active) return;
+  if (half || !active) return;
 
   // output k = 4 f + i of row tile fm: row m0 + 16 fm + 4g + i, column band * 64 + 16 f + u
 #pragma unroll
@@ -639,12 +679,20 @@ int mfq_fm(int64_t M, int64_t groups) {
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 
-struct QuadPlan { int fm; int64_t groups, mgroups, nsplit, tps; };
+// Where 16-row work items of four bands number fewer than this, more than 16 rows take
+// two-band items (BW = 2) instead (measured on MI355X, 70B-shaped batched decode: the M = 64
+// pass 10.18 -> 9.53 ms, M = 32 8.10 -> 7.85 ms; at M = 16 slower, 7.47 -> 7.60 ms).
+constexpr int64_t kMfqTwoBandBelow = 256;
+
+struct QuadPlan { int fm, bw; int64_t groups, mgroups, nsplit, tps; };
 
 QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
-  const int64_t KT = K / 64, bands = N / 64, groups = (bands + 3) / 4;
+  const int64_t KT = K / 64, bands = N / 64;
+  int64_t groups = (bands + 3) / 4;
   const int fm = mfq_fm(M, groups);
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
+  const int bw = (fm == 1 && M > 16 && groups * mgroups < kMfqTwoBandBelow) ? 2 : 4;
+  if (bw == 2) groups = (bands + 1) / 2;
   // K is split until about `target` workgroups; a split spans whole ring turns where the
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
   const int64_t target = 256;
@@ -656,7 +704,7 @@ QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
   if (M * N > kAccCap) nsplit = 1;
   if (nsplit == 1) tps = KT;   // no split words: sum q (w + 1) fits int32 for K <= 65536
   // (nsplit <= KT / 12 <= 86 < kMaxIntSplits: a split word never overflows its count)
-  return {fm, groups, mgroups, nsplit, tps};
+  return {fm, bw, groups, mgroups, nsplit, tps};
 }
 
 // Staged-q kernel: four bands and 16 fm rows per workgroup.
@@ -670,12 +718,14 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, p.tps);
   const int64_t nwork = groups * mgroups * nsplit;   // one workgroup per item, 8 | grid
   const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
-  if (fm == 1)
-    hipLaunchKernelGGL((tern_mfq_kernel<1>), grid, dim3(256), 0, s, a, rowsum);
+  if (fm == 1 && p.bw == 2)
+    hipLaunchKernelGGL((tern_mfq_kernel<1, 2>), grid, dim3(256), 0, s, a, rowsum);
+  else if (fm == 1)
+    hipLaunchKernelGGL((tern_mfq_kernel<1, 4>), grid, dim3(256), 0, s, a, rowsum);
   else if (fm == 2)
-    hipLaunchKernelGGL((tern_mfq_kernel<2>), grid, dim3(256), 0, s, a, rowsum);
+    hipLaunchKernelGGL((tern_mfq_kernel<2, 4>), grid, dim3(256), 0, s, a, rowsum);
   else
-    hipLaunchKernelGGL((tern_mfq_kernel<3>), grid, dim3(256), 0, s, a, rowsum);
+    hipLaunchKernelGGL((tern_mfq_kernel<3, 4>), grid, dim3(256), 0, s, a, rowsum);
   return hipGetLastError();
 }
 
