@@ -679,11 +679,6 @@ int mfq_fm(int64_t M, int64_t groups) {
   return (M > 16 && M <= 64 && groups * ((M + 31) / 32) >= 192) ? 2 : 1;
 }
 
-// Where 16-row work items of four bands number fewer than this, more than 16 rows take
-// two-band items (BW = 2) instead (measured on MI355X, 70B-shaped batched decode: the M = 64
-// pass 10.18 -> 9.53 ms, M = 32 8.10 -> 7.85 ms; at M = 16 slower, 7.47 -> 7.60 ms).
-constexpr int64_t kMfqTwoBandBelow = 256;
-
 struct QuadPlan { int fm, bw; int64_t groups, mgroups, nsplit, tps; };
 
 QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
@@ -691,11 +686,15 @@ QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
   int64_t groups = (bands + 3) / 4;
   const int fm = mfq_fm(M, groups);
   const int64_t mgroups = (M + 16 * fm - 1) / (16 * fm);
-  const int bw = (fm == 1 && M > 16 && groups * mgroups < kMfqTwoBandBelow) ? 2 : 4;
-  if (bw == 2) groups = (bands + 1) / 2;
   // K is split until about `target` workgroups; a split spans whole ring turns where the
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
   const int64_t target = 256;
+  // Where 16-row items of four bands would split K, more than 16 rows take two-band items
+  // (BW = 2: each band's range in two halves met in LDS) and need half the splits (measured on
+  // MI355X, 70B-shaped batched decode at M = 64: o 17.4 -> 12.6 us, down 32.2 -> 30.1 us; q|k|v,
+  // not split, was slower as 320 two-band items, 17.9 against 16.7 us; at M = 16 slower)
+  const int bw = (fm == 1 && M > 16 && 2 * groups * mgroups <= target) ? 2 : 4;
+  if (bw == 2) groups = (bands + 1) / 2;
   int64_t nsplit = std::max<int64_t>(1, target / (groups * mgroups));
   const int64_t turn = kQC * kQRing;
   int64_t tps = (KT + nsplit - 1) / nsplit;
