@@ -352,10 +352,10 @@ constexpr int kRsrcWord3 = 0x00020000;     // raw buffer resource, 32-bit elemen
 
 // 48-row tiles are held to 168 VGPRs (three workgroups per CU instead of two): a 3B-shaped
 // prefill then runs its work items in one round instead of one and a half.
-// BW = 2: a work item is two bands, and each band's K range is split in two halves taken by
-// two waves (waves 2 and 3 take the second halves, with their own q chunks in LDS); the
-// halves' sums meet in LDS. Twice the work items of BW = 4 without split words, for row
-// tiles that would leave CUs idle.
+// BW = 2 or 1: a work item is BW bands, and each band's K range is split in 4 / BW parts taken
+// by as many waves (wave w + BW p takes part p of band w, with its own q chunks in LDS); the
+// parts' sums meet in LDS in part order. 4 / BW times the work items of BW = 4 without split
+// words, for row tiles that would otherwise split K across workgroups.
 template <int FM, int BW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM == 3 ? 3 : 1)))
 void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
@@ -364,11 +364,11 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
   constexpr int KS = 4 / BW;                       // K halves per band
   constexpr int kHT = 256 / KS;                    // threads per half
   constexpr int kSegs = kRows * kQC * 4 / kHT;     // 16-byte pieces of q per thread per chunk
-  static_assert(BW == 4 || BW == 2, "four bands, or two bands in two halves");
+  static_assert(BW == 4 || BW == 2 || BW == 1, "four bands, or fewer with K in 4 / BW parts");
   static_assert(kSegs >= 1 && (kRows * kQC * 4) % kHT == 0, "q chunk copy");
   constexpr int kQBuf = kRows * kQPitch;           // one staged chunk of q
   constexpr int kStBytes = 4 * 16 * kStRow * 4;    // result rows of the epilogue
-  constexpr int kRedBytes = KS > 1 ? BW * FM * 16 * 64 * 4 : 0;   // second halves' sums
+  constexpr int kRedBytes = (KS - 1) * BW * FM * 16 * 64 * 4;   // the other parts' sums
   constexpr int kLds = 2 * KS * kQBuf > kStBytes + kRedBytes ? 2 * KS * kQBuf : kStBytes + kRedBytes;
   __shared__ __attribute__((aligned(16))) int8_t lds[kLds];   // q chunks, then results
   const int tid = threadIdx.x, lane = tid & 63;
@@ -496,25 +496,33 @@ void tern_mfq_kernel(const TernArgs a, const int32_t* __restrict__ rowsum) {
     }
   }
   if constexpr (KS > 1) {
-    // the second halves' sums join the first halves', lane for lane
+    // the later parts' sums join the first part's, lane for lane, in part order
     __syncthreads();                        // every wave is done with the q chunks
-    int* red = reinterpret_cast<int*>(lds + kStBytes) + wave * FM * 16 * 64;
+    int* red = reinterpret_cast<int*>(lds + kStBytes);
+    auto slot = [&](int part) __attribute__((always_inline)) {
+      return red + ((part - 1) * BW + wave) * FM * 16 * 64;
+    };
     if (half) {
+      int* dst = slot(half);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int f = 0; f < 4; ++f)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[((fm * 4 + f) * 4 + i) * 64 + lane] = acc[fm][f][i];
+          for (int i = 0; i < 4; ++i) dst[((fm * 4 + f) * 4 + i) * 64 + lane] = acc[fm][f][i];
     }
     __syncthreads();
     if (!half) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+      for (int part = 1; part < KS; ++part) {
+        const int* src = slot(part);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[fm][f][i] += red[((fm * 4 + f) * 4 + i) * 64 + lane];
+          for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[fm][f][i] += src[((fm * 4 + f) * 4 + i) * 64 + lane];
+      }
     }
   }
   // Without a K split the integers leave through LDS as whole rows: each wave stages its
@@ -689,12 +697,15 @@ QuadPlan plan_mf_quad(int64_t M, int64_t N, int64_t K) {
   // K is split until about `target` workgroups; a split spans whole ring turns where the
   // range allows (no padded chunks) and at most kMfMaxSplitTiles tiles (split word bias)
   const int64_t target = 256;
-  // Where 16-row items of four bands would split K, more than 16 rows take two-band items
-  // (BW = 2: each band's range in two halves met in LDS) and need half the splits (measured on
-  // MI355X, 70B-shaped batched decode at M = 64: o 17.4 -> 12.6 us, down 32.2 -> 30.1 us; q|k|v,
-  // not split, was slower as 320 two-band items, 17.9 against 16.7 us; at M = 16 slower)
-  const int bw = (fm == 1 && M > 16 && 2 * groups * mgroups <= target) ? 2 : 4;
-  if (bw == 2) groups = (bands + 1) / 2;
+  // Where 16-row items of four bands would split K, more than 16 rows take items of two bands
+  // (each band's range in two halves met in LDS), or of one band (four quarters) where even
+  // those would split, and need fewer splits (measured on MI355X, 70B-shaped batched decode:
+  // at M = 64 o 17.4 -> 12.6 us, down 32.2 -> 30.1 us, the pass 10.20 -> 9.50 ms; at M = 32,
+  // one-band o and down, the pass 8.11 -> 7.85 -> 7.51 ms; q|k|v at M = 64, not split, was
+  // slower as 320 two-band items, 17.9 against 16.7 us; at M = 16 slower)
+  const int bw = (fm == 1 && M > 16 && 2 * groups * mgroups <= target)
+                     ? (4 * groups * mgroups <= target ? 1 : 2) : 4;
+  groups = (bands + bw - 1) / bw;
   int64_t nsplit = std::max<int64_t>(1, target / (groups * mgroups));
   const int64_t turn = kQC * kQRing;
   int64_t tps = (KT + nsplit - 1) / nsplit;
@@ -717,7 +728,9 @@ hipError_t launch_mf_quad(const int8_t* q, const float* gamma, const int32_t* ro
   const TernArgs a = mf_args(q, gamma, wmf, beta, beta_len, M, N, K, y, acc_out, ws_acc, p.tps);
   const int64_t nwork = groups * mgroups * nsplit;   // one workgroup per item, 8 | grid
   const dim3 grid(static_cast<unsigned>((nwork + 7) / 8 * 8));
-  if (fm == 1 && p.bw == 2)
+  if (fm == 1 && p.bw == 1)
+    hipLaunchKernelGGL((tern_mfq_kernel<1, 1>), grid, dim3(256), 0, s, a, rowsum);
+  else if (fm == 1 && p.bw == 2)
     hipLaunchKernelGGL((tern_mfq_kernel<1, 2>), grid, dim3(256), 0, s, a, rowsum);
   else if (fm == 1)
     hipLaunchKernelGGL((tern_mfq_kernel<1, 4>), grid, dim3(256), 0, s, a, rowsum);
