@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 //     values its wave quantises in the first chunk, then the wave's first weight batch, so
 //     HBM streaming runs through steps 2-3 (vector loads complete in issue order, so the
 //     x-dependent steps never wait for weights); the ring's other batches follow between
-//     the tiles of step 3;
+//     the tiles of step 3, one after every kIssueGap tiles;
 //  2. gamma: every workgroup reduces |x| over the whole row. For finite fp16 the magnitude
 //     order equals the integer order of the bits with the sign cleared, so this is an
 //     integer max over masked bit patterns (no conversions); a maximum >= 0x7C00 flags
@@ -135,12 +135,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // workgroup's K range: loads past the range return zero without a memory access, so the
 // stream is issued ahead unconditionally (no clamped re-reads at the end of a range).
 // The integer results are identical to bl_quant_act_int8 followed by the GEMV.
-constexpr int kBatch = 4;                   // tiles per register batch
-constexpr int kRing = 4;                    // register batches per wave
+constexpr int kBatch = 2;                   // tiles per register batch
+constexpr int kRing = 8;                    // register batches per wave
 constexpr int kChunk = 64;                  // tiles whose planes sit in LDS at once
 constexpr int kFW = 4;                      // waves (bands) per workgroup
 
 constexpr int kPerWave = kChunk / kFW;      // tiles each wave quantises per chunk
+constexpr int kMinSplitTiles = 4;           // a K split of the fused kernel spans >= 4 tiles
+// Ring shape and issue order, measured on MI355X (70B-shaped decode pass at M = 1, A/B runs
+// of the whole pass on one box): with four 4-tile batches, all of them before gamma 4.82 ms,
+// one per quantised tile 4.34 ms, one per 2 / 3 / 4 tiles 4.30 / 4.29 / 4.33 ms, none before
+// gamma 4.40 ms (weight requests issued sooner queue ahead of the x reads that gamma and the
+// quantiser wait on); eight 2-tile batches, one per quantised tile, 4.24 against 4.28 ms for
+// the best 4 x 4 order (finer batches: the loop waits for two tiles at a time, and the ring
+// is refilled in smaller steps); eight 4-tile batches 4.84 ms, sixteen 1-tile ones 4.38 ms.
+constexpr int kIssueGap = 1;        // quantised tiles per issued batch of the ring
 static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit elements
 // Weights are read once per pass: non-temporal loads (the nt cache policy) keep them from
@@ -268,7 +277,8 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       if constexpr (decltype(first)::value) {
-        if (j + 1 < kRing) load_batch(w[j + 1], (j + 1) * kBatch);
+        if (j % kIssueGap == kIssueGap - 1 && j / kIssueGap + 1 < kRing)
+          load_batch(w[j / kIssueGap + 1], (j / kIssueGap + 1) * kBatch);
       }
       const int tt = c0 + wave + kFW * j;
       if (tt < c1) {
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
       }
     }
   };
-  static_assert(kRing - 1 <= kPerWave, "the ring is issued within the first chunk");
+  static_assert(kIssueGap * (kRing - 1) <= kPerWave, "the ring is issued within the first chunk");
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int c1 = min(t1, c0 + kChunk);
     if (c0 == t0) {
@@ -365,7 +375,7 @@ GemvFusedPlan plan_gemv_fused(int M, int64_t N, int64_t K) {
   const int64_t target = bands < 512 ? 256 : 512;
   int64_t nsplit = target / groups;   // never above the target: a partial extra wave of
                                       // workgroups would run after all the others
-  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kBatch));
+  nsplit = std::min<int64_t>(nsplit, std::max<int64_t>(1, KT / kMinSplitTiles));
   nsplit = std::max<int64_t>(nsplit, 1);
   if (static_cast<int64_t>(M) * N > kAccCap || K > kMaxIntSplitK) nsplit = 1;
   nsplit = std::min<int64_t>(nsplit, kMaxIntSplits);
