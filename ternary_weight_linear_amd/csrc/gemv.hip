@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 //     values its wave quantises in the first chunk, then the wave's first weight batch, so
 //     HBM streaming runs through steps 2-3 (vector loads complete in issue order, so the
 //     x-dependent steps never wait for weights); the ring's other batches follow between
-//     the tiles of step 3, one after every kIssueGap tiles;
+//     the tiles of step 3, one per tile;
 //  2. gamma: every workgroup reduces |x| over the whole row. For finite fp16 the magnitude
 //     order equals the integer order of the bits with the sign cleared, so this is an
 //     integer max over masked bit patterns (no conversions); a maximum >= 0x7C00 flags
@@ -146,10 +146,12 @@ constexpr int kMinSplitTiles = 4;           // a K split of the fused kernel spa
 // of the whole pass on one box): with four 4-tile batches, all of them before gamma 4.82 ms,
 // one per quantised tile 4.34 ms, one per 2 / 3 / 4 tiles 4.30 / 4.29 / 4.33 ms, none before
 // gamma 4.40 ms (weight requests issued sooner queue ahead of the x reads that gamma and the
-// quantiser wait on); eight 2-tile batches, one per quantised tile, 4.24 against 4.28 ms for
-// the best 4 x 4 order (finer batches: the loop waits for two tiles at a time, and the ring
-// is refilled in smaller steps); eight 4-tile batches 4.84 ms, sixteen 1-tile ones 4.38 ms.
-constexpr int kIssueGap = 1;        // quantised tiles per issued batch of the ring
+// quantiser wait on); eight 2-tile batches, one before gamma and one per quantised tile, 4.24
+// against 4.28 ms for the best 4 x 4 order (finer batches: the loop waits for two tiles at a
+// time, and the ring is refilled in smaller steps); eight 4-tile batches 4.84 ms, sixteen
+// 1-tile ones 4.38 ms; of the eight 2-tile batches, one / two / three before gamma (then one
+// per quantised tile) 4.28 / 4.25 / 4.34 ms, two before gamma and two per tile 4.33 ms.
+constexpr int kPreGamma = 2;        // ring batches issued before gamma; then one per tile
 static_assert(kChunk % (kRing * kBatch) == 0, "a chunk holds whole ring turns");
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit elements
 // Weights are read once per pass: non-temporal loads (the nt cache policy) keep them from
@@ -224,10 +226,11 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
   }
   uint16_t xq[kPerWave][MR];
   load_x(xq, t0, min(t1, t0 + kChunk));
-  load_batch(w[0], 0);   // the rest of the ring is issued between the quantised tiles: a wave
-                         // issues its loads in order, and the vector memory path takes
-                         // ~16 cycles per 1 KiB load, so issuing them here would hold the
-                         // gamma fold back
+  // the first kPreGamma batches; the rest of the ring is issued between the quantised tiles: a
+  // wave issues its loads in order, and the vector memory path takes ~16 cycles per 1 KiB
+  // load, so issuing them here would hold the gamma fold back
+#pragma unroll
+  for (int r = 0; r < kPreGamma; ++r) load_batch(w[r], r * kBatch);
 
   // gamma_m = max |x_m| over the whole row (NaN if the row holds NaN/inf)
   float g[MR], rg[MR];
@@ -277,8 +280,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       if constexpr (decltype(first)::value) {
-        if (j % kIssueGap == kIssueGap - 1 && j / kIssueGap + 1 < kRing)
-          load_batch(w[j / kIssueGap + 1], (j / kIssueGap + 1) * kBatch);
+        if (j + kPreGamma < kRing) load_batch(w[j + kPreGamma], (j + kPreGamma) * kBatch);
       }
       const int tt = c0 + wave + kFW * j;
       if (tt < c1) {
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(64 * kFW) void gemv_fused_kernel(
       }
     }
   };
-  static_assert(kIssueGap * (kRing - 1) <= kPerWave, "the ring is issued within the first chunk");
+  static_assert(kRing - kPreGamma <= kPerWave, "the ring is issued within the first chunk");
   for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int c1 = min(t1, c0 + kChunk);
     if (c0 == t0) {
