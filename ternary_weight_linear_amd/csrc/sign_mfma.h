@@ -281,8 +281,9 @@ __global__ __launch_bounds__(256) void sign_mfma_kernel(const SignMfmaArgs a) {
 // A workgroup of kStWaves waves owns NF 16-column fragments of a band (NF = 4: the whole
 // band; NF = 1: fragment f0, so that a layer of few bands still fills the chip without
 // splitting K) and a range of 128-input tiles. It stages x (M rows) and g of its range in
-// LDS with all threads at once and issues every sign word its waves need in the same burst
-// (the lane's S1-128 record, or only word f0 of it), so a wave waits for memory about once
+// LDS with all threads at once and issues the sign words its waves need in one burst (the
+// lane's S1-128 record, or only word f0 of it; with one fragment per workgroup, part of the burst
+// after the staging barrier), so a wave waits for memory about once
 // instead of once per tile or two; then it multiplies: A = x from LDS (lanes of rows past M
 // read row M - 1; those output rows are never stored), B = g from LDS with the sign bits
 // assigned, one v_mfma_f32_16x16x32_f16 per fragment and 32-input slice. The waves' sums
@@ -324,7 +325,8 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
   const int t1 = min(KT, t0 + a.tiles_per_split);
   const int nt = max(t1 - t0, 0);
 
-  // 1. issue the staging loads (x rows, then g), then every sign word of this wave's tiles.
+  // 1. issue the staging loads (x rows, then g), then the sign words of this wave's tiles (with
+  // one fragment per workgroup, part of them after the staging barrier).
   // Every load is unconditional (indices past the range are clamped into it): loads under
   // branches made the compiler wait for each one before issuing the next.
   static_assert(!XG || PW == 4, "registers: x of four tiles per wave");
@@ -348,42 +350,50 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
   sm_u32x4 xv[XG ? PW : 1][4];
   const uint16_t* xg_row = a.x + static_cast<int64_t>(min(r16, M - 1)) * a.K + 8 * grp;
   const uint32_t soff = 16u * lane + 4u * static_cast<uint32_t>(f0);
+  // the sign words (and, at 5..16 rows, x) of the wave's tile j
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int t = min(first + kStWaves * j, t1 - 1);
+    const char* rec0 = reinterpret_cast<const char*>(a.p0) + ((band * KT + t) << 10);
+    const char* rec1 = reinterpret_cast<const char*>(a.p1) + ((band * KT + t) << 10);
+    if constexpr (NF == 4) {
+      const sm_u32x4 r0 = sm_load<sm_u32x4>(rec0, soff);
 #pragma unroll
-  for (int j = 0; j < PW; ++j) {
-    {
-      const int t = min(first + kStWaves * j, t1 - 1);
-      const char* rec0 = reinterpret_cast<const char*>(a.p0) + ((band * KT + t) << 10);
-      const char* rec1 = reinterpret_cast<const char*>(a.p1) + ((band * KT + t) << 10);
-      if constexpr (NF == 4) {
-        const sm_u32x4 r0 = sm_load<sm_u32x4>(rec0, soff);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) w0[j][f] = r0[f];
-        if constexpr (RES) {
-          const sm_u32x4 r1 = sm_load<sm_u32x4>(rec1, soff);
-#pragma unroll
-          for (int f = 0; f < 4; ++f) w1[j][f] = r1[f];
-        }
-      } else {
-        // non-temporal (measured on MI355X, 4096^2 at M = 1 / 16: 4.21 -> 3.89 / 7.74 -> 7.49 us;
-        // for the whole-band mapping it was slower)
-        w0[j][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rec0 + soff));
-        if constexpr (RES) w1[j][0] = sm_load<uint32_t>(rec1, soff);
-      }
-      if constexpr (XG) {
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-          xv[j][sl] = *reinterpret_cast<const sm_u32x4*>(xg_row + static_cast<int64_t>(t) * 128 + 32 * sl);
-      }
+      for (int f = 0; f < 4; ++f) w0[j][f] = r0[f];
       if constexpr (RES) {
+        const sm_u32x4 r1 = sm_load<sm_u32x4>(rec1, soff);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int64_t ci = (band * 64 + 16 * (NF == 4 ? f : f0) + r16) * KT + t;
-          c0[j][f] = a.a0[ci];
-          c1[j][f] = a.a1[ci];
-        }
+        for (int f = 0; f < 4; ++f) w1[j][f] = r1[f];
+      }
+    } else {
+      // non-temporal (measured on MI355X, 4096^2 at M = 1 / 16: 4.21 -> 3.89 / 7.74 -> 7.49 us;
+      // for the whole-band mapping it was slower)
+      w0[j][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rec0 + soff));
+      if constexpr (RES) w1[j][0] = sm_load<uint32_t>(rec1, soff);
+    }
+    if constexpr (XG) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        xv[j][sl] = *reinterpret_cast<const sm_u32x4*>(xg_row + static_cast<int64_t>(t) * 128 + 32 * sl);
+    }
+    if constexpr (RES) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int64_t ci = (band * 64 + 16 * (NF == 4 ? f : f0) + r16) * KT + t;
+        c0[j][f] = a.a0[ci];
+        c1[j][f] = a.a1[ci];
       }
     }
-  }
+  };
+  // One fragment per workgroup: part of the burst goes out behind the staging loads and the
+  // rest after the staging barrier, so that the staging reads of every workgroup are not
+  // queued behind all of the sign words (measured on MI355X, 256-layer graph pools, us per
+  // layer, whole burst first -> half / three quarters / a quarter before the barrier:
+  // OneBit 4096^2 M = 1 3.92 -> 3.74 / 3.81 / 4.00, M = 16 7.48 -> 7.24 / 7.11 / 7.19,
+  // residual 4096^2 M = 1 6.58 -> 5.96 / 6.00 / 6.05); the whole-band mapping (NF = 4) keeps
+  // the whole burst first (28672 x 8192 at M = 1: 14.7 against 15.3 us with half).
+  constexpr int kEarly = NF == 4 ? PW : (XG ? 3 * PW / 4 : PW / 2);
+#pragma unroll
+  for (int j = 0; j < kEarly; ++j) issue(j);
   // 2. staged pieces to LDS: x row m at m * nt * 128 halves, g after the M rows
   if constexpr (kStage) {
 #pragma unroll
@@ -393,6 +403,8 @@ __global__ __launch_bounds__(64 * kStWaves) void sign_staged_kernel(const SignMf
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int j = kEarly; j < PW; ++j) issue(j);
 
   // 3. products: lane (grp, r16) feeds row min(r16, M - 1) of x and column 16 f + r16
   const uint16_t* xrow = st + static_cast<int64_t>(min(r16, M - 1)) * nt * 128 + 8 * grp;
