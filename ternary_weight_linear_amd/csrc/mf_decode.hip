@@ -52,7 +52,11 @@ constexpr int mfd_max_tiles() { return 48 * 1024 / (MR * 64); }
 // quantisation steps whose x is loaded with the first weights (more where a range holds
 // many rows: each later step waits for loads of its own)
 constexpr int mfd_xr(int MR) { return MR >= 8 ? 8 : 2; }
-constexpr int kPre = 1;    // weight batches issued before gamma is folded
+// Weight batches issued before gamma is folded: one up to four rows; none from eight rows on,
+// where every workgroup folds eight or more rows of x and weight requests queued ahead of those
+// reads delay the fold (measured on MI355X, 70B-shaped decode passes, ms: M = 8 6.08-6.13 ->
+// 6.04-6.07, M = 16 7.47 -> 7.36-7.41; at M = 1 none before gamma was slower, 3.93 against 3.79)
+constexpr int mfd_pre(int MR) { return MR >= 8 ? 0 : 1; }
 
 // Split-K hand-off of a lane's MR outputs (rows m < M, bit m of `live`, one column): one
 // split word per output, or per pair of rows where the split count allows (half the
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(64 * kMW) void mf_decode_kernel(
     uint64_t* __restrict__ ws_acc, int tiles_per_split) {
   constexpr int kMaxTiles = mfd_max_tiles<MR>();
   constexpr int kXR = mfd_xr(MR);
+  constexpr int kPre = mfd_pre(MR);
   __shared__ __attribute__((aligned(16))) int8_t qb[kMaxTiles * MR * 64];
   __shared__ uint32_t red_max[kMW][MR];
   __shared__ int rsum[MR];
